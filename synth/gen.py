@@ -1,0 +1,235 @@
+"""Seeded generators for the synthetic workloads (no arithmetic of the method here).
+
+All float inputs are drawn as float32 N(0, 1) from NumPy's PCG64 and rounded to
+bfloat16 with round-to-nearest-even; indexer weights stay float32.  Planting
+only edits indexer keys (never the latent): one entry of each planted block gets
+the key c * q_h* (h* = the indexer head with the largest weight), so that
+block's score stands clear of the unplanted ones.  ``plant_tight`` instead puts
+the planted scores just above the best unplanted block, using a scoring
+function supplied by the caller.
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "rng_for", "bf16_rne", "bf16_to_f32", "normal_bf16", "DecodeInputs",
+    "decode_inputs", "choose_blocks", "plant_dominant", "plant_tight",
+    "plant_groups", "layer_query", "prefill_inputs",
+]
+
+D = 512
+DI = 64
+
+
+def rng_for(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def bf16_rne(x):
+    """float32 array -> bfloat16 bit patterns (uint16), round to nearest even (finite inputs)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_bf16(rng, shape, chunk=1 << 24):
+    """N(0,1) float32 draws rounded to bfloat16, drawn in chunks to bound memory."""
+    out = np.empty(int(np.prod(shape)), dtype=np.uint16)
+    for s in range(0, out.size, chunk):
+        e = min(out.size, s + chunk)
+        out[s:e] = bf16_rne(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def _positive_weights(rng, shape):
+    """float32 N(0,1) weights, redrawn per row until at least one entry is positive."""
+    w = rng.standard_normal(shape, dtype=np.float32)
+    flat = w.reshape(-1, shape[-1])
+    for r in range(flat.shape[0]):
+        while flat[r].max() <= 0:
+            flat[r] = rng.standard_normal(shape[-1], dtype=np.float32)
+    return flat.reshape(shape)
+
+
+@dataclass
+class DecodeInputs:
+    latent: np.ndarray      # u16 [B][N][512]  entries to append to the MXFP4 cache
+    keys: np.ndarray        # u16 [B][N][64]   indexer keys, one per entry
+    q: np.ndarray           # u16 [B][Q][H][512]
+    q_idx: np.ndarray       # u16 [B][Q][Hi][64]
+    w: np.ndarray           # f32 [B][Q][Hi]
+    swa: np.ndarray         # u16 [B][W][512]  sliding-window tokens (K = V)
+    swa_len: np.ndarray     # i32 [B]
+    n_entries: np.ndarray   # i32 [B]
+    planted: list = field(default_factory=list)   # per sequence: planted block ids
+
+
+def choose_blocks(rng, nb_present, count, exclude=None, pool=None):
+    """``count`` distinct block ids drawn from ``pool`` (default all present blocks) minus ``exclude``."""
+    cand = np.arange(nb_present) if pool is None else np.asarray(pool)
+    if exclude is not None and len(exclude):
+        cand = np.setdiff1d(cand, np.asarray(exclude))
+    count = min(count, cand.size)
+    return np.sort(rng.choice(cand, size=count, replace=False))
+
+
+def _lead_head(w_row):
+    return int(np.argmax(np.asarray(w_row)))
+
+
+def _entry_in_block(rng, blk, n_entries):
+    hi = min(8, n_entries - 8 * blk)
+    return 8 * blk + int(rng.integers(0, hi))
+
+
+def plant_dominant(keys, n_entries, q_idx_row, w_row, blocks, rng, c=3.0):
+    """In place: one present entry of each block in ``blocks`` gets key bf16(c * q_h*)."""
+    h = _lead_head(w_row)
+    u = bf16_to_f32(q_idx_row[h])
+    key = bf16_rne(np.float32(c) * u)
+    for b in blocks:
+        keys[_entry_in_block(rng, int(b), n_entries)] = key
+    return np.asarray(blocks)
+
+
+def plant_tight(keys, n_entries, q_idx_row, w_row, blocks, rng, score_fn, margin=0.5, step=0.01):
+    """In place: planted blocks score a little above the best unplanted block.
+
+    ``score_fn(keys_u16 [n][64]) -> float64 [n]`` gives entry scores for this row.
+    Planted block r (in the given order) gets one entry with key bf16(c_r * q_h*)
+    where c_r = (T + margin + step * r) / score(q_h*) and T is the best score of
+    any entry outside the planted blocks.  The caller checks the resulting gap.
+    """
+    blocks = np.asarray(blocks)
+    n = int(n_entries)
+    s = np.asarray(score_fn(keys[:n]), dtype=np.float64)
+    planted_entry = np.zeros(n, dtype=bool)
+    for b in blocks:
+        planted_entry[8 * b: min(8 * b + 8, n)] = True
+    T = s[~planted_entry].max() if (~planted_entry).any() else 0.0
+    order = np.argsort(-np.asarray(w_row))
+    for h in order:
+        u = bf16_to_f32(q_idx_row[h])
+        su = float(score_fn(bf16_rne(u)[None, :])[0])
+        if su > 0:
+            break
+    else:
+        raise ValueError("no indexer head gives a positive planted score")
+    for r, b in enumerate(rng.permutation(blocks)):
+        c = np.float32((max(T, 0.0) + margin + step * r) / su)
+        keys[_entry_in_block(rng, int(b), n)] = bf16_rne(c * u)
+    return blocks
+
+
+def plant_groups(keys, n_entries, q_idx_row, w_row, groups, mu=1.0):
+    """In place: every present key of each group (512 entries) gets mu * q_h* / 8 added."""
+    h = _lead_head(w_row)
+    u = bf16_to_f32(q_idx_row[h]) * np.float32(mu / 8.0)
+    for g in groups:
+        lo, hi = 512 * int(g), min(512 * int(g) + 512, int(n_entries))
+        if hi > lo:
+            keys[lo:hi] = bf16_rne(bf16_to_f32(keys[lo:hi]) + u[None, :])
+    return np.asarray(groups)
+
+
+def layer_query(rng, B, Q, H, Hi):
+    """One layer's own attention query and indexer query/weights."""
+    q = normal_bf16(rng, (B, Q, H, D))
+    q_idx = normal_bf16(rng, (B, Q, Hi, DI))
+    w = _positive_weights(rng, (B, Q, Hi))
+    return q, q_idx, w
+
+
+def decode_inputs(cfg, seed=None, plant="dominant", score_fn=None, n_entries=None,
+                  batches=None, c=3.0):
+    """Inputs for a decode workload (Q rows per sequence attend the whole cache).
+
+    plant: "dominant" (scores far above the rest), "tight" (needs ``score_fn(b)``
+    returning a per-sequence entry-score function), or None (no plant).
+    ``n_entries`` overrides the per-sequence entry counts (ragged caches);
+    ``batches`` limits generation to the first ``batches`` sequences.
+    """
+    rng = rng_for(cfg.seed if seed is None else seed)
+    B = cfg.B if batches is None else batches
+    N = cfg.N
+    ne = np.full(B, N, dtype=np.int32) if n_entries is None else np.asarray(n_entries, np.int32)
+    latent = normal_bf16(rng, (B, N, D))
+    keys = normal_bf16(rng, (B, N, DI))
+    q, q_idx, w = layer_query(rng, B, cfg.Q, cfg.H, cfg.Hi)
+    swa = normal_bf16(rng, (B, cfg.W, D))
+    swa_len = np.full(B, cfg.W, dtype=np.int32)
+    planted = []
+    for b in range(B):
+        nbp = (int(ne[b]) + 7) // 8
+        if cfg.top_groups:
+            ngp = (int(ne[b]) + 511) // 512
+            groups = choose_blocks(rng, ngp, cfg.top_groups)
+            plant_groups(keys[b], ne[b], q_idx[b, 0], w[b, 0], groups)
+            pool = (groups[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+            pool = pool[pool < nbp]
+        else:
+            pool = None
+        if plant is None:
+            planted.append(np.zeros(0, dtype=np.int64))
+            continue
+        blocks = choose_blocks(rng, nbp, cfg.K, pool=pool)
+        if plant == "dominant":
+            plant_dominant(keys[b], ne[b], q_idx[b, 0], w[b, 0], blocks, rng, c=c)
+        elif plant == "tight":
+            plant_tight(keys[b], ne[b], q_idx[b, 0], w[b, 0], blocks, rng, score_fn(b))
+        else:
+            raise ValueError(plant)
+        planted.append(blocks)
+    return DecodeInputs(latent, keys, q, q_idx, w, swa, swa_len, ne, planted)
+
+
+def prefill_inputs(cfg, seed=None, q_rows=None, n_dirs=4, c=3.0, beta=1.0):
+    """Inputs for a causal chunk: cfg.prior entries already cached, then cfg.Q new raw tokens.
+
+    The Q query tokens sit at raw positions 2*prior .. 2*prior + Q - 1; the chunk
+    adds Q/2 new entries.  Queries are split into ``n_dirs`` groups; group d's
+    indexer queries share a direction v_d (q_idx = z + beta * v_d), and 2048
+    blocks per group among the prior blocks get one key bf16(c * v_d).  Returns
+    a dict of arrays; ``q_rows`` limits the query rows generated (all positions
+    are kept so the cache is the same).
+    """
+    rng = rng_for(cfg.seed if seed is None else seed)
+    Q = cfg.Q
+    prior = cfg.prior
+    N = prior + Q // 2
+    latent = normal_bf16(rng, (1, N, D))
+    keys = normal_bf16(rng, (1, N, DI))
+    dirs = normal_bf16(rng, (n_dirs, DI))
+    z = rng.standard_normal((Q, cfg.Hi, DI), dtype=np.float32)
+    group = np.arange(Q) % n_dirs
+    qf = z + np.float32(beta) * bf16_to_f32(dirs)[group][:, None, :]
+    q_idx = bf16_rne(qf)[None]
+    w = np.abs(rng.standard_normal((1, Q, cfg.Hi), dtype=np.float32)) + np.float32(0.1)
+    q = normal_bf16(rng, (1, Q, cfg.H, D))
+    nb_prior = prior // 8
+    planted = []
+    used = np.zeros(0, dtype=np.int64)
+    for d in range(n_dirs):
+        blocks = choose_blocks(rng, nb_prior, cfg.K, exclude=used)
+        used = np.concatenate([used, blocks])
+        key = bf16_rne(np.float32(c) * bf16_to_f32(dirs[d]))
+        for b in blocks:
+            keys[0, _entry_in_block(rng, int(b), prior)] = key
+        planted.append(blocks)
+    swa_total = cfg.W + Q
+    swa_pos0 = 2 * prior - cfg.W
+    swa = normal_bf16(rng, (1, swa_total, D))
+    q_pos = (2 * prior + np.arange(Q)).astype(np.int32)[None]
+    if q_rows is not None:
+        sel = np.asarray(q_rows)
+        q, q_idx, w, q_pos = q[:, sel], q_idx[:, sel], w[:, sel], q_pos[:, sel]
+    return dict(latent=latent, keys=keys, q=q, q_idx=q_idx, w=w, q_pos=q_pos,
+                swa=swa, swa_len=np.array([swa_total], np.int32),
+                swa_pos0=np.array([swa_pos0], np.int32), prior=prior,
+                n_entries=np.array([N], np.int32), planted=planted)
