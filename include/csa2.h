@@ -1,0 +1,149 @@
+/*
+ * csa2.h -- C ABI of the CSA2 sparse-decode attention library for MI355X (gfx950).
+ *
+ * The operation: compressed sparse attention over an FP4 global latent cache.
+ * One 512-d latent per compressed entry is the key and the value for every
+ * query head; each entry merges two adjacent raw positions (paper-digest.app,
+ * "DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache Compression", Core
+ * Mechanics, "Compressed along three axes").  An indexer selects up to 2048
+ * blocks of 8 entries per query, every layer also attends its own sliding
+ * window, and layers run in Full / Reindex / Reuse modes
+ * (observer.broadside.tech card, same title, Key ideas, "CSA2 with three static
+ * layer modes").  The cache is stored in FP4 (news.promptgoblins.ai, "DeepSeek
+ * Releases V4.1 Flash with 4x KV Cache Compression ...", Details, "FP4 KVCache
+ * precision"); the concrete format here is MXFP4 (OCP Microscaling v1.0:
+ * E2M1 codes, one E8M0 scale per 32 values).
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers unless stated.  The caller owns
+ *    every buffer, including workspaces sized by the *_ws() queries; the
+ *    library allocates nothing and keeps no state, and calls are re-entrant.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work and return; nothing is synchronised.
+ *  - bfloat16 arrays are passed as uint16_t bit patterns.
+ *  - Return value: CSA2_OK (0) or a negative status; argument checks run on
+ *    the host before anything is enqueued, so on error nothing was launched.
+ *    No exception or abort crosses the ABI.  Device data is not validated:
+ *    block ids outside [0, cap/8) (e.g. the -1 padding) are skipped in-kernel.
+ *
+ * Byte layouts (fixed by this header):
+ *  - Latent cache, per sequence: cap/8 block records of CSA2_RECORD_BYTES.
+ *    Record of block b (entries 8b..8b+7): bytes [0,2048) = the 8 entries'
+ *    packed codes, entry-major, 256 B each (byte k: code of dim 2k in the low
+ *    nibble, dim 2k+1 in the high nibble; code = sign<<3 | E2M1 magnitude
+ *    code); bytes [2048,2176) = the 8 entries' 16 E8M0 scale bytes,
+ *    entry-major (scale g covers dims 32g..32g+31).
+ *  - Indexer keys: bf16 [B][cap][64].  Group sums: fp32 [B][cap/512][64].
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_D 512              /* latent width (K = V)                     */
+#define CSA2_DI 64              /* indexer key / query width                */
+#define CSA2_BLOCK 8            /* entries per selection block              */
+#define CSA2_GROUP_BLOCKS 64    /* blocks per coarse group (two-level)      */
+#define CSA2_RECORD_BYTES 2176  /* bytes per block record                   */
+#define CSA2_MAX_HEADS 128      /* attention heads per row                  */
+#define CSA2_MAX_INDEX_HEADS 16 /* indexer heads                            */
+
+enum {
+    CSA2_OK = 0,
+    CSA2_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misaligned buffer   */
+    CSA2_ERR_UNSUPPORTED = -2,   /* valid but not supported by these kernels    */
+    CSA2_ERR_WS_TOO_SMALL = -3,  /* workspace smaller than the *_ws() query      */
+    CSA2_ERR_LAUNCH = -4         /* the HIP runtime reported a launch error      */
+};
+
+/* Append n_new entries per sequence to the latent cache (MXFP4 quantise + pack).
+ * Encoding per 32-value group: amax = max |x|; sb = clamp(floor(log2 amax) - 2
+ * + 127, 0, 254) (amax = 0 -> 0); codes = |x| / 2^(sb-127) rounded to the E2M1
+ * grid {0,.5,1,1.5,2,3,4,6} to nearest, halfway cases to the even code, above 6
+ * saturating; sign bit copied (also for zero magnitudes).  A group holding a
+ * NaN/Inf gets sb = 255 and zero codes.
+ *   latent      bf16 [B][n_new][512]
+ *   idx_key     bf16 [B][n_new][64] or NULL; copied to key_cache when given
+ *   start_entry int32 [B] (device): entry position of each sequence's first
+ *               new entry; entries at positions >= cap are dropped
+ *   cache       u8 [B][cap/8][2176]; key_cache bf16 [B][cap][64] or NULL
+ *   group_sum   fp32 [B][cap/512][64] or NULL: each new key is added to its
+ *               512-entry group's sum (needs idx_key and cap % 512 == 0)
+ * Bytes of records not covered by new entries are left untouched. */
+int csa2_append_fp4(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry,
+                    int B, int n_new, int cap, uint8_t* cache, uint16_t* key_cache,
+                    float* group_sum, void* stream);
+
+/* Indexer + top-K block selection for B*Q query rows.
+ * Entry score e_j = sum_h w_h * max(0, q_h . k_j) (fp32 accumulation); block
+ * score = max over the block's present (j < n_entries[b]) and visible entries;
+ * a block with none is not a candidate.  Visibility: with q_pos, entry j is
+ * visible to raw position t iff 2j+1 <= t; without, all present entries are.
+ * Keeps the top_k candidates by (score desc, block id asc) and writes them
+ * ascending, padded with -1, plus their count.
+ * Two-level (top_groups > 0, needs group_sum, q_pos == NULL): group g = blocks
+ * [64g, 64g+64) scores its mean key (group_sum / present count); the best
+ * top_groups groups are kept, and blocks are scored only inside them.
+ *   q_idx bf16 [B][Q][Hi][64]; w fp32 [B][Q][Hi]; key_cache bf16 [B][cap][64]
+ *   n_entries int32 [B]; q_pos int32 [B][Q] or NULL
+ *   idx int32 [B][Q][top_k]; count int32 [B][Q]
+ *   ws: >= csa2_index_topk_ws(B, Q, cap, top_groups) bytes, 256-B aligned */
+int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* key_cache,
+                    const float* group_sum, const int32_t* n_entries, const int32_t* q_pos,
+                    int B, int Q, int Hi, int cap, int top_k, int top_groups,
+                    int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
+size_t csa2_index_topk_ws(int B, int Q, int cap, int top_groups);
+
+/* Top-K of precomputed scores (the selection step of csa2_index_topk).
+ * scores fp32 [rows][n]; -inf or NaN marks a non-candidate.  Same rule and
+ * output format as csa2_index_topk: idx int32 [rows][k] ascending, -1 padded;
+ * count int32 [rows].  n <= 65536. */
+int csa2_topk(const float* scores, int rows, int n, int k, int32_t* idx, int32_t* count,
+              void* stream);
+
+/* Sparse multi-head attention over the selected blocks of the latent cache.
+ * For each row r = (b, q) and head h: z_j = scale * (q_h . V_j) over the
+ * present, visible entries j of the blocks idx[r][0..count[r]); V_j = the
+ * dequantised entry; o = softmax(z) V (fp32), lse = log sum exp z.  An empty
+ * selection gives o = 0, lse = -inf.  bf16 MFMA with fp32 accumulation; the
+ * softmax weights are rounded to bf16 before the value product.
+ *   q bf16 [B][Q][H][512]; cache as above; idx int32 [B][Q][top_k];
+ *   count int32 [B][Q]; n_entries int32 [B]; q_pos int32 [B][Q] or NULL
+ *   o fp32 [B][Q][H][512]; lse fp32 [B][Q][H] (natural log)
+ *   ws: >= csa2_sparse_attn_ws(B, Q, H, top_k) bytes (split-K partials) */
+int csa2_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
+                     const int32_t* count, const int32_t* n_entries, const int32_t* q_pos,
+                     int B, int Q, int H, int cap, int top_k, float scale,
+                     float* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+size_t csa2_sparse_attn_ws(int B, int Q, int H, int top_k);
+
+/* Sliding-window branch and log-sum-exp merge with the sparse branch.
+ * Window slot i of sequence b holds raw position swa_pos0[b] + i (swa_pos0
+ * NULL = 0), for i < swa_len[b] <= Lw.  The query at raw position t (q_pos, or
+ * NULL = the newest held token) attends positions [t-W+1, t] that are held.
+ * Branch (o_w, lse_w) is computed as in csa2_sparse_attn (K = V = bf16
+ * window tokens), then out = e^(lse_s-L) o_s + e^(lse_w-L) o_w with
+ * L = logaddexp(lse_s, lse_w) (both -inf: out = 0, L = -inf).
+ *   swa_kv bf16 [B][Lw][512]; o_sparse/out fp32 [B][Q][H][512] (may alias);
+ *   lse_sparse/lse_out fp32 [B][Q][H] (may alias)
+ *   ws: >= csa2_swa_merge_ws(B, Q, H, W) bytes */
+int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa_len,
+                   const int32_t* swa_pos0, const int32_t* q_pos, int B, int Q, int H, int W,
+                   int Lw, float scale, const float* o_sparse, const float* lse_sparse,
+                   float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream);
+size_t csa2_swa_merge_ws(int B, int Q, int H, int W);
+
+/* Human-readable name of a status code (static string, host). */
+const char* csa2_status_str(int status);
+/* Library version: major * 10000 + minor * 100 + patch. */
+int csa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

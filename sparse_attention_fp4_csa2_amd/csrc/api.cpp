@@ -1,0 +1,222 @@
+// C ABI of the CSA2 sparse-decode library: argument checks, workspace
+// carving, and kernel launch sequencing.  Every check runs on the host before
+// anything is enqueued; the library allocates nothing and keeps no state.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/csa2.h"
+#include "launch.h"
+
+using namespace csa2;
+
+namespace {
+
+constexpr size_t WS_ALIGN = 256;
+
+inline size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int launch_status(int rc) { return rc == 0 ? CSA2_OK : CSA2_ERR_LAUNCH; }
+
+// Index/top-K workspace pieces.
+struct IndexWs {
+  size_t scores;      // fp32 [rows][n_score]
+  size_t gscores;     // fp32 [rows][cap/512]
+  size_t gsel;        // int32 [rows][top_groups]
+  size_t gcount;      // int32 [rows]
+  size_t total;
+};
+
+IndexWs index_ws_layout(int B, int Q, int cap, int top_groups) {
+  const size_t rows = (size_t)B * Q;
+  IndexWs l{};
+  const size_t n_score = top_groups > 0 ? (size_t)top_groups * CSA2_GROUP_BLOCKS : (size_t)cap / CSA2_BLOCK;
+  size_t off = 0;
+  l.scores = off; off += align_up(rows * n_score * sizeof(float));
+  if (top_groups > 0) {
+    l.gscores = off; off += align_up(rows * (size_t)(cap / 512) * sizeof(float));
+    l.gsel = off; off += align_up(rows * (size_t)top_groups * sizeof(int32_t));
+    l.gcount = off; off += align_up(rows * sizeof(int32_t));
+  }
+  l.total = off;
+  return l;
+}
+
+int attn_n_tiles(int top_k) { return (top_k + 3) / 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_str(int status) {
+  switch (status) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_INVALID_ARG: return "invalid argument";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CSA2_ERR_WS_TOO_SMALL: return "workspace too small";
+    case CSA2_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int csa2_version(void) { return 10000; }
+
+int csa2_append_fp4(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry,
+                    int B, int n_new, int cap, uint8_t* cache, uint16_t* key_cache,
+                    float* group_sum, void* stream) {
+  if (!latent || !start_entry || !cache) return CSA2_ERR_INVALID_ARG;
+  if (B <= 0 || n_new < 0 || cap <= 0 || cap % CSA2_BLOCK != 0) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(latent, 16) || !aligned(cache, 16)) return CSA2_ERR_INVALID_ARG;
+  if ((idx_key == nullptr) != (key_cache == nullptr)) return CSA2_ERR_INVALID_ARG;
+  if (idx_key && (!aligned(idx_key, 16) || !aligned(key_cache, 16))) return CSA2_ERR_INVALID_ARG;
+  if (group_sum) {
+    if (!idx_key) return CSA2_ERR_INVALID_ARG;
+    if (cap % 512 != 0) return CSA2_ERR_UNSUPPORTED;
+    if (!aligned(group_sum, 16)) return CSA2_ERR_INVALID_ARG;
+  }
+  if (n_new == 0) return CSA2_OK;
+  return launch_status(launch_append(latent, idx_key, start_entry, B, n_new, cap, cache, key_cache,
+                                     group_sum, as_stream(stream)));
+}
+
+size_t csa2_index_topk_ws(int B, int Q, int cap, int top_groups) {
+  if (B <= 0 || Q <= 0 || cap <= 0) return 0;
+  return index_ws_layout(B, Q, cap, top_groups).total;
+}
+
+int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* key_cache,
+                    const float* group_sum, const int32_t* n_entries, const int32_t* q_pos,
+                    int B, int Q, int Hi, int cap, int top_k, int top_groups,
+                    int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  if (!q_idx || !w || !key_cache || !n_entries || !idx || !count) return CSA2_ERR_INVALID_ARG;
+  if (B <= 0 || Q <= 0 || Hi <= 0 || cap <= 0 || top_k <= 0 || top_groups < 0)
+    return CSA2_ERR_INVALID_ARG;
+  if (cap % CSA2_BLOCK != 0 || top_k > cap / CSA2_BLOCK) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q_idx, 16) || !aligned(key_cache, 16)) return CSA2_ERR_INVALID_ARG;
+  if (Hi > CSA2_MAX_INDEX_HEADS) return CSA2_ERR_UNSUPPORTED;
+  if ((size_t)cap / CSA2_BLOCK > 65536) return CSA2_ERR_UNSUPPORTED;
+  const IndexWs l = index_ws_layout(B, Q, cap, top_groups);
+  if (!ws || ws_bytes < l.total) return CSA2_ERR_WS_TOO_SMALL;
+  if (!aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base + l.scores);
+  hipStream_t st = as_stream(stream);
+  const int rows = B * Q;
+  if (top_groups == 0) {
+    int rc = launch_index_scores(q_idx, w, key_cache, n_entries, q_pos, B, Q, Hi, cap, nullptr, 0,
+                                 scores, st);
+    if (rc) return CSA2_ERR_LAUNCH;
+    return launch_status(launch_topk(scores, rows, cap / CSA2_BLOCK, top_k, nullptr, 0, idx, count, st));
+  }
+  // two-level
+  if (!group_sum || q_pos) return CSA2_ERR_UNSUPPORTED;
+  if (cap % 512 != 0) return CSA2_ERR_UNSUPPORTED;
+  const int G = cap / 512;
+  if (top_groups > G) return CSA2_ERR_INVALID_ARG;
+  if ((size_t)top_groups * CSA2_GROUP_BLOCKS > 65536) return CSA2_ERR_UNSUPPORTED;
+  float* gscores = reinterpret_cast<float*>(base + l.gscores);
+  int32_t* gsel = reinterpret_cast<int32_t*>(base + l.gsel);
+  int32_t* gcount = reinterpret_cast<int32_t*>(base + l.gcount);
+  int rc = launch_group_scores(q_idx, w, group_sum, n_entries, B, Q, Hi, cap, gscores, st);
+  if (!rc) rc = launch_topk(gscores, rows, G, top_groups, nullptr, 0, gsel, gcount, st);
+  if (!rc) rc = launch_index_scores(q_idx, w, key_cache, n_entries, nullptr, B, Q, Hi, cap, gsel,
+                                    top_groups, scores, st);
+  if (!rc) rc = launch_topk(scores, rows, top_groups * CSA2_GROUP_BLOCKS, top_k, gsel, top_groups,
+                            idx, count, st);
+  return launch_status(rc);
+}
+
+int csa2_topk(const float* scores, int rows, int n, int k, int32_t* idx, int32_t* count,
+              void* stream) {
+  if (!scores || !idx || !count) return CSA2_ERR_INVALID_ARG;
+  if (rows <= 0 || n <= 0 || k <= 0) return CSA2_ERR_INVALID_ARG;
+  if (n > 65536) return CSA2_ERR_UNSUPPORTED;
+  return launch_status(launch_topk(scores, rows, n, k, nullptr, 0, idx, count, as_stream(stream)));
+}
+
+size_t csa2_sparse_attn_ws(int B, int Q, int H, int top_k) {
+  if (B <= 0 || Q <= 0 || H <= 0 || top_k <= 0) return 0;
+  const int rows = B * Q;
+  const int s = attn_splits(rows, H, attn_n_tiles(top_k));
+  if (s <= 1) return 0;
+  return align_up((size_t)rows * s * H * CSA2_D * sizeof(float)) +
+         align_up((size_t)rows * s * H * sizeof(float));
+}
+
+int csa2_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
+                     const int32_t* count, const int32_t* n_entries, const int32_t* q_pos,
+                     int B, int Q, int H, int cap, int top_k, float scale,
+                     float* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !cache || !idx || !count || !n_entries || !o || !lse) return CSA2_ERR_INVALID_ARG;
+  if (B <= 0 || Q <= 0 || H <= 0 || cap <= 0 || top_k <= 0) return CSA2_ERR_INVALID_ARG;
+  if (cap % CSA2_BLOCK != 0 || !(scale > 0.f) || !isfinite(scale)) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(o, 16)) return CSA2_ERR_INVALID_ARG;
+  if (H > CSA2_MAX_HEADS) return CSA2_ERR_UNSUPPORTED;
+  const int rows = B * Q;
+  const int splits = attn_splits(rows, H, attn_n_tiles(top_k));
+  const size_t need = csa2_sparse_attn_ws(B, Q, H, top_k);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WS_TOO_SMALL;
+  if (need > 0 && !aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
+  AttnParams p{};
+  p.q = q; p.cache = cache; p.idx = idx; p.count = count; p.n_entries = n_entries;
+  p.top_k = top_k; p.cap = cap; p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows;
+  p.splits = splits;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t st = as_stream(stream);
+  if (splits == 1) {
+    p.o_out = o; p.lse_out = lse;
+    return launch_status(launch_attention(p, true, st));
+  }
+  float* o_part = static_cast<float*>(ws);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                             align_up((size_t)rows * splits * H * CSA2_D * sizeof(float)));
+  p.o_out = o_part; p.lse_out = lse_part;
+  int rc = launch_attention(p, true, st);
+  if (!rc) rc = launch_combine(o_part, lse_part, rows, splits, H, nullptr, nullptr, o, lse, st);
+  return launch_status(rc);
+}
+
+size_t csa2_swa_merge_ws(int B, int Q, int H, int W) {
+  if (B <= 0 || Q <= 0 || H <= 0 || W <= 0) return 0;
+  const int rows = B * Q;
+  const int s = attn_splits(rows, H, (W + 31) / 32);
+  return align_up((size_t)rows * s * H * CSA2_D * sizeof(float)) +
+         align_up((size_t)rows * s * H * sizeof(float));
+}
+
+int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa_len,
+                   const int32_t* swa_pos0, const int32_t* q_pos, int B, int Q, int H, int W,
+                   int Lw, float scale, const float* o_sparse, const float* lse_sparse,
+                   float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !swa_kv || !swa_len || !o_sparse || !lse_sparse || !out || !lse_out)
+    return CSA2_ERR_INVALID_ARG;
+  if (B <= 0 || Q <= 0 || H <= 0 || W <= 0 || Lw <= 0) return CSA2_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(swa_kv, 16) || !aligned(o_sparse, 16) || !aligned(out, 16))
+    return CSA2_ERR_INVALID_ARG;
+  if (H > CSA2_MAX_HEADS) return CSA2_ERR_UNSUPPORTED;
+  const size_t need = csa2_swa_merge_ws(B, Q, H, W);
+  if (!ws || ws_bytes < need) return CSA2_ERR_WS_TOO_SMALL;
+  if (!aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
+  const int rows = B * Q;
+  const int splits = attn_splits(rows, H, (W + 31) / 32);
+  AttnParams p{};
+  p.q = q; p.swa = swa_kv; p.swa_len = swa_len; p.swa_pos0 = swa_pos0; p.W = W; p.Lw = Lw;
+  p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows; p.splits = splits;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  float* o_part = static_cast<float*>(ws);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                             align_up((size_t)rows * splits * H * CSA2_D * sizeof(float)));
+  p.o_out = o_part; p.lse_out = lse_part;
+  hipStream_t st = as_stream(stream);
+  int rc = launch_attention(p, false, st);
+  if (!rc) rc = launch_combine(o_part, lse_part, rows, splits, H, o_sparse, lse_sparse, out, lse_out, st);
+  return launch_status(rc);
+}
+
+}  // extern "C"

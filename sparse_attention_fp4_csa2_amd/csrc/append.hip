@@ -1,0 +1,123 @@
+// Cache append: MXFP4 quantise + pack of new latent entries, indexer-key copy,
+// group-sum update.
+//
+// Storage of the global latent cache in FP4 follows the news.promptgoblins.ai
+// summary (Details, "FP4 KVCache precision") and the thelatestinai.com
+// abstract; the format is MXFP4 as in the OCP Microscaling Formats v1.0
+// specification (E2M1 elements, one E8M0 scale per 32 values).  Each entry is a
+// merged pair of raw positions (paper-digest.app page, Core Mechanics).
+//
+// One wave quantises one 512-value entry: lane l owns values [8l, 8l+8), four
+// lanes form a 32-value scale group.  All decisions are exact integer
+// arithmetic on the bf16 bit patterns, so the packed bytes are reproducible
+// bit for bit.
+#include "device.h"
+#include "launch.h"
+
+namespace csa2 {
+
+// floor(log2 |x|) for a nonzero finite bf16 magnitude pattern (sign cleared).
+__device__ __forceinline__ int floor_log2_bf16(uint32_t mag) {
+  uint32_t ef = mag >> 7;
+  if (ef) return (int)ef - 127;
+  // subnormal: mag = m * 2^-133 with 1 <= m < 128
+  return (31 - __builtin_clz(mag)) - 133;
+}
+
+// E2M1 magnitude code (0..7) of |x| / 2^(sb-127), round to nearest, halfway to
+// the even code, saturating at 6.  mag = bf16 magnitude bits of x.
+__device__ __forceinline__ uint32_t e2m1_code(uint32_t mag, int sb) {
+  uint32_t ef = mag >> 7;
+  uint32_t sig = ef ? (0x80u | (mag & 0x7Fu)) : (mag & 0x7Fu);
+  int ex = ef ? (int)ef : 1;
+  // |x|/X * 4 = sig * 2^-u with u = sb + 5 - ex; halfway points *4 are the
+  // integers 1 3 5 7 10 14 20
+  int u = sb + 5 - ex;
+  if (u < 0) return 7;           // far above 6: saturate
+  if (u >= 9) return 0;          // below 0.125: rounds to 0
+  const uint32_t T[7] = {1u, 3u, 5u, 7u, 10u, 14u, 20u};
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) c += (sig > (T[i] << u)) ? 1u : 0u;
+  if (c < 7 && sig == (T[c] << u) && (c & 1u)) c += 1;   // exact tie -> even code
+  return c;
+}
+
+__global__ __launch_bounds__(256) void append_fp4_kernel(
+    const uint16_t* __restrict__ latent, const uint16_t* __restrict__ idx_key,
+    const int32_t* __restrict__ start_entry, int n_new, int cap,
+    uint8_t* __restrict__ cache, uint16_t* __restrict__ key_cache) {
+  const int b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave;          // new entry index
+  if (i >= n_new) return;
+  const long long j = (long long)start_entry[b] + i;   // cache entry position
+  if (j < 0 || j >= cap) return;
+
+  const uint16_t* src = latent + ((size_t)b * n_new + i) * D + lane * 8;
+  uint4 raw = *reinterpret_cast<const uint4*>(src);
+  uint32_t v[8] = {raw.x & 0xFFFFu, raw.x >> 16, raw.y & 0xFFFFu, raw.y >> 16,
+                   raw.z & 0xFFFFu, raw.z >> 16, raw.w & 0xFFFFu, raw.w >> 16};
+  // group amax as an integer on the magnitude bits (monotonic for finite bf16)
+  uint32_t amax = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) amax = max(amax, v[k] & 0x7FFFu);
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
+  const bool nonfinite = amax >= 0x7F80u;
+  int sb = 0;
+  if (!nonfinite && amax) sb = min(max(floor_log2_bf16(amax) - 2 + 127, 0), 254);
+
+  uint32_t packed = 0;
+  if (!nonfinite) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t code = ((v[k] >> 15) << 3) | e2m1_code(v[k] & 0x7FFFu, sb);
+      packed |= code << (4 * k);
+    }
+  }
+  uint8_t* rec = cache + ((size_t)b * (cap / BLOCK) + (size_t)(j / BLOCK)) * RECORD;
+  const int slot = (int)(j % BLOCK);
+  *reinterpret_cast<uint32_t*>(rec + slot * 256 + lane * 4) = packed;
+  if ((lane & 3) == 0) rec[SCALE_OFF + slot * 16 + (lane >> 2)] = (uint8_t)(nonfinite ? 255 : sb);
+
+  if (idx_key != nullptr && key_cache != nullptr && lane < 8) {
+    const uint4* ks = reinterpret_cast<const uint4*>(idx_key + ((size_t)b * n_new + i) * DI) + lane;
+    uint4* kd = reinterpret_cast<uint4*>(key_cache + ((size_t)b * cap + (size_t)j) * DI) + lane;
+    *kd = *ks;
+  }
+}
+
+// Group sums: one 64-thread block per (sequence, touched group); thread d adds
+// the new keys of that group to dimension d in entry order (deterministic).
+__global__ __launch_bounds__(64) void group_sum_kernel(
+    const uint16_t* __restrict__ idx_key, const int32_t* __restrict__ start_entry,
+    int n_new, int cap, float* __restrict__ group_sum) {
+  const int b = blockIdx.y;
+  const int d = threadIdx.x;
+  const long long s0 = start_entry[b];
+  const long long g0 = s0 / GROUP_ENTRIES;
+  const long long g = g0 + blockIdx.x;
+  const long long lo = max(s0, g * GROUP_ENTRIES);
+  const long long hi = min(min(s0 + n_new, (g + 1) * GROUP_ENTRIES), (long long)cap);
+  if (s0 < 0 || lo >= hi) return;
+  float acc = 0.f;
+  for (long long j = lo; j < hi; ++j)
+    acc += bf16_to_f32(idx_key[((size_t)b * n_new + (size_t)(j - s0)) * DI + d]);
+  group_sum[((size_t)b * (cap / GROUP_ENTRIES) + (size_t)g) * DI + d] += acc;
+}
+
+int launch_append(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry,
+                  int B, int n_new, int cap, uint8_t* cache, uint16_t* key_cache,
+                  float* group_sum, hipStream_t stream) {
+  dim3 grid((n_new + 3) / 4, B);
+  append_fp4_kernel<<<grid, 256, 0, stream>>>(latent, idx_key, start_entry, n_new, cap, cache,
+                                              key_cache);
+  if (group_sum != nullptr) {
+    dim3 g2((n_new + GROUP_ENTRIES - 1) / GROUP_ENTRIES + 1, B);
+    group_sum_kernel<<<g2, 64, 0, stream>>>(idx_key, start_entry, n_new, cap, group_sum);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace csa2

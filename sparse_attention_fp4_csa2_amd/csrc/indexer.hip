@@ -1,0 +1,187 @@
+// Sparse indexer: entry scores, fused block max, and the coarse group stage.
+//
+// The pages name the indexer and its output -- up to 2048 blocks of 8 per
+// query, rescored per layer in Reindex mode, two-level ("hierarchical") to trim
+// decoder indexing (observer.broadside.tech card, Key ideas, "CSA2 with three
+// static layer modes") -- but print no formula.  The score used here:
+//   e_j = sum_h w_h * max(0, q_h . k_j),  block score = max over its visible,
+//   present entries; coarse group score = the same formula on the group's mean key.
+//
+// The entry scores are a genuine [Hi x 64] x [64 x N] contraction per query
+// row, done on v_mfma_f32_16x16x32_bf16: A = the row's indexer query (heads
+// padded to 16), B = 16 keys per MFMA.  The ReLU, weights, head sum and the
+// 8-entry block max run in the epilogue, so entry scores never reach memory.
+// Keys stream once from HBM with 32-byte loads per lane.
+#include "device.h"
+#include "launch.h"
+
+namespace csa2 {
+
+namespace {
+
+constexpr int CH_FLAT = 2048;   // entries per workgroup (flat)
+constexpr int CH_GROUP = 512;   // entries per workgroup (one coarse group)
+constexpr int UNROLL = 4;       // 16-entry tiles in flight per wave
+constexpr int MAX_HI = 16;      // indexer heads (rows of the A operand)
+
+__device__ __forceinline__ floatx4 mfma16(uint4 a, uint4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+}  // namespace
+
+// grid: (chunks, rows).  Flat: chunk x covers entries [x*CH, x*CH + CH) and
+// writes block scores at [row][x*CH/8 ...] of a row of length n_out = cap/8.
+// Group-restricted: chunk x covers group gsel[row][x] and writes at
+// [row][x*64 ...] of a row of length n_out = 64 * n_groups_sel.
+template <int CH>
+__global__ __launch_bounds__(256) void index_scores_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ key_cache, const int32_t* __restrict__ n_entries,
+    const int32_t* __restrict__ q_pos, int Q, int Hi, int cap,
+    const int32_t* __restrict__ gsel, int n_groups_sel, int n_out, float* __restrict__ scores) {
+  const int x = blockIdx.x, row = blockIdx.y;
+  const int b = row / Q;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15;            // entry within a 16-entry tile / head row of A
+  const int kg = lane >> 4;           // k-group: dims [16kg, 16kg+16)
+
+  int e0;
+  if (gsel) {
+    const int g = gsel[(size_t)row * n_groups_sel + x];
+    e0 = g < 0 ? -1 : g * GROUP_ENTRIES;
+  } else {
+    e0 = x * CH;
+  }
+  float* out = scores + (size_t)row * n_out + (size_t)x * (CH / BLOCK);
+  const int ne = n_entries[b];
+  const int limit_vis = q_pos ? ((q_pos[row] - 1) >> 1) + 1 : 0x7FFFFFFF;   // visible iff j < limit
+  const int jmax = min(min(ne, cap), limit_vis);          // entries [0, jmax) count
+
+  if (e0 < 0) {
+    // unused group slot: no candidates
+    for (int i = threadIdx.x; i < CH / BLOCK; i += 256) out[i] = -__builtin_inff();
+    return;
+  }
+
+  // A fragments: head n (< Hi), dims [16kg + 8ks, +8)
+  uint4 qa[2];
+  const size_t qoff = ((size_t)row * Hi + n) * DI + 16 * kg;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    qa[ks] = n < Hi ? *reinterpret_cast<const uint4*>(q_idx + qoff + 8 * ks) : make_uint4(0, 0, 0, 0);
+  // weights of the 4 heads this lane's accumulator rows hold: 4kg + i
+  float wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * kg + i;
+    wv[i] = h < Hi ? w[(size_t)row * Hi + h] : 0.f;
+  }
+
+  constexpr int PER_WAVE = CH / 4;              // entries per wave
+  constexpr int TILES = PER_WAVE / 16;
+  const int wbase = e0 + wave * PER_WAVE;
+  const uint16_t* kbase = key_cache + (size_t)b * cap * DI;
+
+  for (int t0 = 0; t0 < TILES; t0 += UNROLL) {
+    uint4 kb[UNROLL][2];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int j = wbase + 16 * (t0 + u) + n;
+      if (j < jmax) {
+        const uint4* kp = reinterpret_cast<const uint4*>(kbase + (size_t)j * DI + 16 * kg);
+        kb[u][0] = kp[0];
+        kb[u][1] = kp[1];
+      } else {
+        kb[u][0] = make_uint4(0, 0, 0, 0);
+        kb[u][1] = kb[u][0];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      floatx4 acc = floatx4{};
+      acc = mfma16(qa[0], kb[u][0], acc);
+      acc = mfma16(qa[1], kb[u][1], acc);
+      // acc[i]: head 4kg + i, entry n
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part += wv[i] * fmaxf(acc[i], 0.f);
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      const int j = wbase + 16 * (t0 + u) + n;
+      float s = j < jmax ? part : -__builtin_inff();
+      s = fmaxf(s, __shfl_xor(s, 1, 64));
+      s = fmaxf(s, __shfl_xor(s, 2, 64));
+      s = fmaxf(s, __shfl_xor(s, 4, 64));
+      const int local_blk = (wave * PER_WAVE + 16 * (t0 + u) + n) / BLOCK;
+      if ((lane == 0 || lane == 8) && x * (CH / BLOCK) + local_blk < n_out) out[local_blk] = s;
+    }
+  }
+}
+
+// Coarse scores: one workgroup per row, one thread per group at a time.
+__global__ __launch_bounds__(256) void group_scores_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const float* __restrict__ group_sum, const int32_t* __restrict__ n_entries, int Q, int Hi,
+    int cap, float* __restrict__ gscores) {
+  __shared__ float qs[MAX_HI][DI];
+  __shared__ float ws[MAX_HI];
+  const int row = blockIdx.x, b = row / Q;
+  for (int i = threadIdx.x; i < Hi * DI; i += 256)
+    qs[i / DI][i % DI] = bf16_to_f32(q_idx[(size_t)row * Hi * DI + i]);
+  if (threadIdx.x < Hi) ws[threadIdx.x] = w[(size_t)row * Hi + threadIdx.x];
+  __syncthreads();
+  const int G = cap / GROUP_ENTRIES;
+  const int ne = min(n_entries[b], cap);
+  for (int g = threadIdx.x; g < G; g += 256) {
+    const int cnt = min(GROUP_ENTRIES, ne - g * GROUP_ENTRIES);
+    float s = -__builtin_inff();
+    if (cnt > 0) {
+      const float inv = 1.f / (float)cnt;
+      const float4* gs = reinterpret_cast<const float4*>(group_sum + ((size_t)b * G + g) * DI);
+      float mean[DI];
+#pragma unroll
+      for (int d4 = 0; d4 < DI / 4; ++d4) {
+        const float4 v = gs[d4];
+        mean[4 * d4] = v.x * inv; mean[4 * d4 + 1] = v.y * inv;
+        mean[4 * d4 + 2] = v.z * inv; mean[4 * d4 + 3] = v.w * inv;
+      }
+      s = 0.f;
+      for (int h = 0; h < Hi; ++h) {
+        float dot = 0.f;
+#pragma unroll
+        for (int d = 0; d < DI; ++d) dot += qs[h][d] * mean[d];
+        s += ws[h] * fmaxf(dot, 0.f);
+      }
+    }
+    gscores[(size_t)row * G + g] = s;
+  }
+}
+
+int launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* key_cache,
+                        const int32_t* n_entries, const int32_t* q_pos, int B, int Q, int Hi,
+                        int cap, const int32_t* gsel, int n_groups_sel, float* scores,
+                        hipStream_t stream) {
+  const int rows = B * Q;
+  if (gsel) {
+    dim3 grid(n_groups_sel, rows);
+    index_scores_kernel<CH_GROUP><<<grid, 256, 0, stream>>>(
+        q_idx, w, key_cache, n_entries, q_pos, Q, Hi, cap, gsel, n_groups_sel,
+        n_groups_sel * (CH_GROUP / BLOCK), scores);
+  } else {
+    dim3 grid((cap + CH_FLAT - 1) / CH_FLAT, rows);
+    index_scores_kernel<CH_FLAT><<<grid, 256, 0, stream>>>(
+        q_idx, w, key_cache, n_entries, q_pos, Q, Hi, cap, nullptr, 0, cap / BLOCK, scores);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_group_scores(const uint16_t* q_idx, const float* w, const float* group_sum,
+                        const int32_t* n_entries, int B, int Q, int Hi, int cap, float* gscores,
+                        hipStream_t stream) {
+  group_scores_kernel<<<B * Q, 256, 0, stream>>>(q_idx, w, group_sum, n_entries, Q, Hi, cap,
+                                                 gscores);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace csa2

@@ -1,0 +1,60 @@
+// Internal launch entry points (host side of each .hip translation unit).
+// Arguments are validated by the C-ABI layer before these are called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+int launch_append(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry,
+                  int B, int n_new, int cap, uint8_t* cache, uint16_t* key_cache,
+                  float* group_sum, hipStream_t stream);
+
+// Block scores fp32 [rows][n_out]: flat (gsel == nullptr: n_out = cap/8) or
+// restricted to the selected groups gsel [rows][n_groups_sel] (n_out = 64 per group).
+int launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* key_cache,
+                        const int32_t* n_entries, const int32_t* q_pos, int B, int Q, int Hi,
+                        int cap, const int32_t* gsel, int n_groups_sel, float* scores,
+                        hipStream_t stream);
+
+// Coarse group scores fp32 [rows][cap/512] from group sums.
+int launch_group_scores(const uint16_t* q_idx, const float* w, const float* group_sum,
+                        const int32_t* n_entries, int B, int Q, int Hi, int cap, float* gscores,
+                        hipStream_t stream);
+
+// Top-k per row of scores [rows][n] -> idx [rows][k] ascending, -1 padded, count [rows].
+// With gsel != nullptr, position p maps to block gsel[row][p / 64] * 64 + p % 64.
+int launch_topk(const float* scores, int rows, int n, int k, const int32_t* gsel, int n_gsel,
+                int32_t* idx, int32_t* count, hipStream_t stream);
+
+struct AttnParams {
+  const uint16_t* q;        // [rows][H][512]
+  // MXFP4 source
+  const uint8_t* cache;     // [B][cap/8][2176]
+  const int32_t* idx;       // [rows][top_k]
+  const int32_t* count;     // [rows]
+  const int32_t* n_entries; // [B]
+  int top_k, cap;
+  // bf16 window source
+  const uint16_t* swa;      // [B][Lw][512]
+  const int32_t* swa_len;   // [B]
+  const int32_t* swa_pos0;  // [B] or null
+  int W, Lw;
+  // common
+  const int32_t* q_pos;     // [rows] or null
+  int Q, H, rows, splits;
+  float scale_log2;         // scale * log2(e)
+  float* o_out;             // [rows][splits][H][512] (final o when splits == 1)
+  float* lse_out;           // [rows][splits][H]
+};
+
+int attn_splits(int rows, int H, int n_tiles);
+int launch_attention(const AttnParams& p, bool fp4_source, hipStream_t stream);
+
+// Merge split partials (and an optional extra branch) -> out [rows][H][512], lse [rows][H].
+int launch_combine(const float* o_part, const float* lse_part, int rows, int splits, int H,
+                   const float* o_ext, const float* lse_ext, float* out, float* lse_out,
+                   hipStream_t stream);
+
+}  // namespace csa2

@@ -1,0 +1,103 @@
+"""Cross-layer modes composed from the four library calls (host orchestration only).
+
+The pages define three static layer modes (observer.broadside.tech card, Key
+ideas, "CSA2 with three static layer modes"): Full makes the global KV and
+indexes it; Reindex reuses an earlier layer's KV but rescores it with the
+layer's own indexer query; Reuse reuses both the KV and the earlier layer's
+top-K indices.  Every layer has its own query and its own sliding window.
+Here a mode is just which calls run: Full/Reindex = csa2_index_topk +
+csa2_sparse_attn + csa2_swa_merge; Reuse = the last two on the earlier
+layer's index buffer, passed unchanged.
+"""
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+SCALE = 1.0 / math.sqrt(512.0)
+
+
+@dataclass
+class LatentCache:
+    """Device state shared by the layers: MXFP4 records, indexer keys, group sums."""
+    records: torch.Tensor     # u8 [B][cap/8][2176]
+    keys: torch.Tensor        # bf16 [B][cap][64]
+    group_sum: torch.Tensor   # fp32 [B][cap/512][64] or None
+    n_entries: torch.Tensor   # int32 [B]
+
+    @property
+    def cap(self):
+        return self.keys.shape[1]
+
+    @staticmethod
+    def empty(B, cap, device="cuda", with_groups=False):
+        rec = torch.zeros(B, cap // 8, _lib.RECORD_BYTES, dtype=torch.uint8, device=device)
+        keys = torch.zeros(B, cap, 64, dtype=torch.bfloat16, device=device)
+        gs = torch.zeros(B, cap // 512, 64, dtype=torch.float32, device=device) if with_groups else None
+        n = torch.zeros(B, dtype=torch.int32, device=device)
+        return LatentCache(rec, keys, gs, n)
+
+    def append(self, latent, keys, stream=None):
+        """Append n_new entries per sequence at each sequence's current end."""
+        start = self.n_entries.clone()
+        _lib.append_fp4(latent, start, self.records, idx_key=keys, key_cache=self.keys,
+                        group_sum=self.group_sum, stream=stream)
+        self.n_entries += latent.shape[1]
+
+
+class LayerBuffers:
+    """Per-layer outputs and workspaces, sized once (the calls themselves allocate nothing)."""
+
+    def __init__(self, B, Q, H, cap, top_k, W, top_groups=0, device="cuda"):
+        self.B, self.Q, self.H, self.cap, self.top_k, self.W = B, Q, H, cap, top_k, W
+        self.top_groups = top_groups
+        dev = device
+        self.idx = torch.empty(B, Q, top_k, dtype=torch.int32, device=dev)
+        self.count = torch.empty(B, Q, dtype=torch.int32, device=dev)
+        self.o = torch.empty(B, Q, H, 512, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(B, Q, H, dtype=torch.float32, device=dev)
+        self.out = torch.empty(B, Q, H, 512, dtype=torch.float32, device=dev)
+        self.lse_out = torch.empty(B, Q, H, dtype=torch.float32, device=dev)
+        self.ws_index = _ws(_lib.index_topk_ws(B, Q, cap, top_groups), dev)
+        self.ws_attn = _ws(_lib.sparse_attn_ws(B, Q, H, top_k), dev)
+        self.ws_swa = _ws(_lib.swa_merge_ws(B, Q, H, W), dev)
+
+
+def _ws(nbytes, dev):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+
+
+def index(buf, cache, q_idx, w, q_pos=None, stream=None):
+    _lib.index_topk(q_idx, w, cache.keys, cache.n_entries, buf.top_k, buf.idx, buf.count,
+                    buf.ws_index, group_sum=cache.group_sum if buf.top_groups else None,
+                    q_pos=q_pos, top_groups=buf.top_groups, stream=stream)
+
+
+def attend(buf, cache, q, swa, swa_len, idx=None, count=None, swa_pos0=None, q_pos=None,
+           scale=SCALE, stream=None):
+    idx = buf.idx if idx is None else idx
+    count = buf.count if count is None else count
+    _lib.sparse_attn(q, cache.records, idx, count, cache.n_entries, scale, buf.o, buf.lse,
+                     ws=buf.ws_attn, q_pos=q_pos, stream=stream)
+    _lib.swa_merge(q, swa, swa_len, buf.W, scale, buf.o, buf.lse, buf.out, buf.lse_out,
+                   buf.ws_swa, swa_pos0=swa_pos0, q_pos=q_pos, stream=stream)
+
+
+def run_layer(mode, buf, cache, q, swa, swa_len, q_idx=None, w=None, prev=None, stream=None):
+    """One decode layer.  mode: "F" (Full), "R" (Reindex) or "U" (Reuse, needs ``prev``).
+
+    Returns the (idx, count) this layer attended; for Reuse they are ``prev``'s
+    buffers themselves, untouched.
+    """
+    if mode in ("F", "R"):
+        index(buf, cache, q_idx, w, stream=stream)
+        attend(buf, cache, q, swa, swa_len, stream=stream)
+        return buf.idx, buf.count
+    if mode == "U":
+        idx, count = prev
+        attend(buf, cache, q, swa, swa_len, idx=idx, count=count, stream=stream)
+        return idx, count
+    raise ValueError(f"unknown mode {mode!r}")
