@@ -42,7 +42,10 @@ namespace csa2 {
 namespace {
 
 constexpr int TILE = 32;              // entries per tile
-constexpr int VROW = 272;             // 16-bit elements per V row (256 + 16: rows 8 banks apart)
+constexpr int VROW = 288;             // 16-bit elements per V row (256 + 32 pad)
+// 16-byte unit u of V row r is stored at unit u ^ ((r >> 2) & 3): with the
+// 288-element stride both the entry-major row writes and the transposed reads
+// are free of LDS bank conflicts.
 constexpr int MAX_SPLIT_BLOCKS = 2048; // selected blocks one workgroup stages in LDS
 constexpr float LAZY_LOG2 = 8.0f;     // rescale only when the max grows by > 2^8
 constexpr int VBIAS = 140;            // V' = V * 2^(VBIAS - vbase): code 6 at vbase -> 6*2^13
@@ -275,9 +278,10 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
     for (int j = 0; j < 4; ++j)
       lds.sred[sbuf][w][j][lane] = floatx4{sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3]};
     // kf[0..7] hold dims 128hh + 64hg + [0,64) (contraction order rotated by hg)
-    uint4* vrow = reinterpret_cast<uint4*>(&lds.vbuf[sbuf][dh][e * VROW + 128 * hh + 64 * hg]);
+    uint16_t* vrow = &lds.vbuf[sbuf][dh][e * VROW + 128 * hh + 64 * hg];
+    const int xw = (e >> 2) & 3;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) vrow[k] = kf[k];
+    for (int k = 0; k < 8; ++k) *reinterpret_cast<uint4*>(vrow + 8 * (k ^ xw)) = kf[k];
   };
   auto raise_base = [&](const Raw& r, int cur) -> int {   // largest valid scale byte of the wave
     int smax = 0;
@@ -377,13 +381,16 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
         const int r0 = 16 * ks2 + 4 * (blk16 >> 1) + (sl >> 2);
-        const uint16_t* vb = &lds.vbuf[buf][dh][r0 * VROW + 16 * (blk16 & 1) + 4 * (sl & 3)];
+        const int u0 = 2 * (blk16 & 1) + ((sl & 3) >> 1);            // unit within each 4-unit group
+        const int x0 = (blk16 >> 1) & 3, x1 = ((blk16 >> 1) + 2) & 3;  // swizzle of rows r0, r0 + 8
+        const uint16_t* vb0 = &lds.vbuf[buf][dh][r0 * VROW + 8 * (u0 ^ x0) + 4 * (sl & 1)];
+        const uint16_t* vb1 = &lds.vbuf[buf][dh][(r0 + 8) * VROW + 8 * (u0 ^ x1) + 4 * (sl & 1)];
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
           vr[ks2][mt][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                                                        (lds_bf16x4*)(vb + 32 * mt)));
+                                                        (lds_bf16x4*)(vb0 + 32 * mt)));
           vr[ks2][mt][1] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                                                        (lds_bf16x4*)(vb + 32 * mt + 8 * VROW)));
+                                                        (lds_bf16x4*)(vb1 + 32 * mt)));
         }
       }
     }
