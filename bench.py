@@ -16,6 +16,7 @@ fp64 oracle on a bounded sample of rows on the host cores.
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -31,6 +32,10 @@ if ROOT not in sys.path:
 METRIC = "sparse-attn decode queries/s and TB/s FP4 KV read; % of HBM/MFMA roofline"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBPS = 8000.0
+# HBM bytes per csa2_sparse_attn call from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# counter runs, with the hash of the kernel source they were taken on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_attn_decode64k.json")
+KERNEL_SRC = os.path.join(ROOT, "sparse_attention_fp4_csa2_amd", "csrc", "attention.hip")
 
 
 def parse():
@@ -41,8 +46,9 @@ def parse():
     ap.add_argument("--config", default="decode64k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with rocprofv3 FETCH/WRITE-derived bytes per launch of the attention kernel")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, run a plain fp32 copy kernel over this many bytes "
+                         "(the calibration point for rocprofv3 FETCH_SIZE / WRITE_SIZE runs)")
     return ap.parse_args()
 
 
@@ -132,9 +138,16 @@ def main():
     idx_bytes = B * N * 128
     idx_gbps = idx_bytes / (t_index * 1e-3) / 1e9
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic = stored_traffic()
 
     result = {
         "metric": METRIC,
@@ -147,7 +160,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4 cache, bf16/fp16 MFMA, fp32 accumulate",
+        "dtype": "fp16",
         "data": "synthetic (seeded N(0,1) bf16, planted relevant blocks)",
         "config": {"workload": f"{cfg.name}: decode, B {B}, H {H}, {N} MXFP4 entries/seq "
                                f"({N // 8} blocks of 8), indexer {cfg.Hi}x64, top-K {K}, window {W}",
@@ -156,7 +169,8 @@ def main():
         "breakdown_ms": {"append": round(t_append, 4), "index_topk": round(t_index, 4),
                          "sparse_attn": round(t_attn, 4), "swa_merge": round(t_swa, 4)},
         "indexer_GBps": round(idx_gbps, 1),
-        "roofline": {"kernel": "csa2_sparse_attn (attention + split combine)", "bound": "mfma",
+        "compute": "MXFP4 cache dequantised to fp16 for fp16 MFMA, fp32 accumulate; window in bf16",
+        "roofline": {"kernel": "csa2_sparse_attn (attention + split-K combine)", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": flops_attn},
@@ -166,6 +180,17 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def stored_traffic():
+    """Measured HBM bytes per csa2_sparse_attn call, or None once the kernel source changed."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    digest = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if rec.get("attention_hip_sha256") != digest:
+        return None
+    return rec.get("bytes_per_call")
 
 
 def cpu_baseline(cfg, x, budget_s):
