@@ -1,24 +1,27 @@
-"""Benchmark: CSA2 sparse-decode step over an MXFP4 latent cache on one MI355X.
+"""Benchmark: CSA2 sparse attention over an MXFP4 latent cache on one MI355X.
 
-One step = the whole hot path for one decode token of every sequence:
-  csa2_append_fp4 (one new entry per sequence) -> csa2_index_topk (indexer +
-  top-K blocks) -> csa2_sparse_attn (gather + dequant + 64-head attention,
-  split-K) -> csa2_swa_merge (sliding window + log-sum-exp merge).
-Default workload: decode at 64K context (32 sequences, 64 heads, 32768 MXFP4
-entries = 4096 blocks of 8 per sequence, 8 x 64 indexer, top-K 2048, window
-512), seeded synthetic N(0,1) inputs with planted relevant blocks.
+One step = the whole hot path over one batch of synthetic input:
+  decode    csa2_append_fp4 (one new entry per sequence) -> per layer:
+            csa2_index_topk (Full / Reindex) -> csa2_sparse_attn -> csa2_swa_merge
+  prefill   csa2_append_fp4 (the chunk's 2048 entries) -> csa2_index_topk (causal,
+            every query row) -> csa2_sparse_attn -> csa2_swa_merge (causal window)
+Default workload (--config decode64k): decode at 64K context, 32 sequences, 64
+heads, 32768 MXFP4 entries = 4096 blocks of 8 per sequence, 8 x 64 indexer,
+top-K 2048, window 512; seeded N(0,1) bf16 inputs with planted relevant blocks.
+Other configs (decode1m, layers128k, prefill, tiny) time the same step shape on
+their own workloads.
 
-Prints ONE JSON line.  `value` = decode queries/s (rows / step time).  The
-`roofline` object covers the dominant call, csa2_sparse_attn (MFMA-bound at 64
-heads): algorithmic FLOPs = 4 * H * (8 * K) * 512 per row, timed with HIP
-events on the stream the library launches on.  `cpu_baseline` times the NumPy
-fp64 oracle on a bounded sample of rows on the host cores.
+Prints ONE JSON line.  `value` = query rows per second (decode queries/s, or
+prefill tokens/s).  `roofline` covers csa2_sparse_attn (attention kernel + its
+split-K combine; MFMA-bound at 64 heads): algorithmic FLOPs = 4 * H * 512 per
+selected visible entry, over the call's mean time from HIP events recorded on
+the stream the library launches on.  `cpu_baseline` times the NumPy fp64
+oracle on a bounded sample of rows on the host cores.
 """
 
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -30,26 +33,197 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "sparse-attn decode queries/s and TB/s FP4 KV read; % of HBM/MFMA roofline"
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
+RECORD = 2176
 # HBM bytes per csa2_sparse_attn call from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # counter runs, with the hash of the kernel source they were taken on
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_attn_decode64k.json")
 KERNEL_SRC = os.path.join(ROOT, "sparse_attention_fp4_csa2_amd", "csrc", "attention.hip")
 
 
-def parse():
+def traffic_file(config):
+    return os.path.join(ROOT, "profiles", f"traffic_sparse_attn_{config}.json")
+
+
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="decode64k")
+    ap.add_argument("--config", default="decode64k",
+                    choices=["tiny", "decode64k", "decode1m", "layers128k", "prefill"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain fp32 copy kernel over this many bytes "
                          "(the calibration point for rocprofv3 FETCH_SIZE / WRITE_SIZE runs)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
+
+
+# ---------------------------------------------------------------------------
+# workloads (device state + one step), shared with the full-size parity tests
+
+
+class DecodeWorkload:
+    """Decode: B sequences, one query row each, through the layers of ``cfg.layers``."""
+
+    def __init__(self, cfg, x, layers, device="cuda"):
+        import torch
+        from sparse_attention_fp4_csa2_amd import _lib, modes
+        self.torch, self._lib, self.modes = torch, _lib, modes
+        self.cfg, self.x, self.layer_inputs = cfg, x, layers
+        B, N = x.latent.shape[0], cfg.N
+        self.B, self.rows = B, B * cfg.Q
+        self.cache = modes.LatentCache.empty(B, cfg.cap, device, with_groups=bool(cfg.top_groups))
+        self.cache.append(_bf(x.latent, device), _bf(x.keys, device))
+        self.swa_len = torch.from_numpy(x.swa_len).to(device)
+        self.layers = []
+        for L in layers:
+            buf = modes.LayerBuffers(B, cfg.Q, cfg.H, cfg.cap, cfg.K, cfg.W,
+                                     top_groups=cfg.top_groups, device=device)
+            self.layers.append(dict(
+                mode=L.mode, buf=buf, q=_bf(L.q, device), swa=_bf(L.swa, device),
+                q_idx=_bf(L.q_idx, device) if L.q_idx is not None else None,
+                w=torch.from_numpy(L.w).to(device) if L.w is not None else None))
+        # decode append: one new entry per sequence, rewritten at the last held
+        # position so every step sees the same cache
+        self.new_lat = _bf(x.latent[:, N - 1:N], device)
+        self.new_key = _bf(x.keys[:, N - 1:N], device)
+        self.start = torch.full((B,), N - 1, dtype=torch.int32, device=device)
+        self.stream = torch.cuda.current_stream()
+
+    def append(self):
+        self._lib.append_fp4(self.new_lat, self.start, self.cache.records, idx_key=self.new_key,
+                             key_cache=self.cache.keys, group_sum=self.cache.group_sum,
+                             stream=self.stream)
+
+    def step(self):
+        self.append()
+        prev = None
+        for L in self.layers:
+            prev = self.modes.run_layer(L["mode"], L["buf"], self.cache, L["q"], L["swa"],
+                                        self.swa_len, q_idx=L["q_idx"], w=L["w"], prev=prev,
+                                        stream=self.stream)
+
+    def calls(self):
+        """name -> (callable, launches per step) for the per-call breakdown."""
+        L0 = self.layers[0]
+        buf = L0["buf"]
+        m, lib, s = self.modes, self._lib, self.stream
+        n_index = sum(1 for L in self.layers if L["mode"] in ("F", "R"))
+        return {
+            "append": (self.append, 1),
+            "index_topk": (lambda: m.index(buf, self.cache, L0["q_idx"], L0["w"], stream=s), n_index),
+            "sparse_attn": (self.sparse_attn_call, len(self.layers)),
+            "swa_merge": (lambda: lib.swa_merge(L0["q"], L0["swa"], self.swa_len, self.cfg.W, m.SCALE,
+                                                buf.o, buf.lse, buf.out, buf.lse_out, buf.ws_swa,
+                                                stream=s), len(self.layers)),
+        }
+
+    def sparse_attn_call(self):
+        L0 = self.layers[0]
+        buf = L0["buf"]
+        self._lib.sparse_attn(L0["q"], self.cache.records, buf.idx, buf.count, self.cache.n_entries,
+                              self.modes.SCALE, buf.o, buf.lse, ws=buf.ws_attn, stream=self.stream)
+
+    def attended_entries(self):
+        """Selected visible entries summed over rows, for the first layer's selection."""
+        counts = self.layers[0]["buf"].count.cpu().numpy()
+        return int(counts.sum()) * 8
+
+
+class PrefillWorkload:
+    """Chunked prefill: Q query tokens after ``prior`` cached entries, causal everywhere."""
+
+    def __init__(self, cfg, p, device="cuda"):
+        import torch
+        from sparse_attention_fp4_csa2_amd import _lib, modes
+        self.torch, self._lib, self.modes = torch, _lib, modes
+        self.cfg, self.p = cfg, p
+        N, prior = int(p["n_entries"][0]), int(p["prior"])
+        Q = p["q"].shape[1]
+        self.B, self.rows = 1, Q
+        self.cache = modes.LatentCache.empty(1, cfg.cap, device)
+        self.cache.append(_bf(p["latent"], device), _bf(p["keys"], device))
+        self.buf = modes.LayerBuffers(1, Q, cfg.H, cfg.cap, cfg.K, cfg.W, device=device)
+        self.q = _bf(p["q"], device)
+        self.q_idx = _bf(p["q_idx"], device)
+        self.w = torch.from_numpy(p["w"]).to(device)
+        self.q_pos = torch.from_numpy(p["q_pos"]).to(device)
+        self.swa = _bf(p["swa"], device)
+        self.swa_len = torch.from_numpy(p["swa_len"]).to(device)
+        self.swa_pos0 = torch.from_numpy(p["swa_pos0"]).to(device)
+        # the chunk's entries, rewritten in place each step
+        self.chunk_lat = _bf(p["latent"][:, prior:N], device)
+        self.chunk_key = _bf(p["keys"][:, prior:N], device)
+        self.start = torch.full((1,), prior, dtype=torch.int32, device=device)
+        self.stream = torch.cuda.current_stream()
+
+    def append(self):
+        self._lib.append_fp4(self.chunk_lat, self.start, self.cache.records, idx_key=self.chunk_key,
+                             key_cache=self.cache.keys, stream=self.stream)
+
+    def index(self):
+        self.modes.index(self.buf, self.cache, self.q_idx, self.w, q_pos=self.q_pos, stream=self.stream)
+
+    def sparse_attn_call(self):
+        b = self.buf
+        self._lib.sparse_attn(self.q, self.cache.records, b.idx, b.count, self.cache.n_entries,
+                              self.modes.SCALE, b.o, b.lse, ws=b.ws_attn, q_pos=self.q_pos,
+                              stream=self.stream)
+
+    def swa_call(self):
+        b = self.buf
+        self._lib.swa_merge(self.q, self.swa, self.swa_len, self.cfg.W, self.modes.SCALE, b.o, b.lse,
+                            b.out, b.lse_out, b.ws_swa, swa_pos0=self.swa_pos0, q_pos=self.q_pos,
+                            stream=self.stream)
+
+    def step(self):
+        self.append()
+        self.index()
+        self.sparse_attn_call()
+        self.swa_call()
+
+    def calls(self):
+        return {"append": (self.append, 1), "index_topk": (self.index, 1),
+                "sparse_attn": (self.sparse_attn_call, 1), "swa_merge": (self.swa_call, 1)}
+
+    def attended_entries(self):
+        """Visible entries of the selected blocks summed over rows (causal masking counted)."""
+        idx = self.buf.idx.cpu().numpy()[0]
+        cnt = self.buf.count.cpu().numpy()[0]
+        qpos = self.p["q_pos"][0]
+        n = int(self.p["n_entries"][0])
+        total = 0
+        for r in range(idx.shape[0]):
+            blk = idx[r, :cnt[r]].astype(np.int64)
+            ent = blk[:, None] * 8 + np.arange(8)[None, :]
+            total += int(((ent < n) & (2 * ent + 1 <= qpos[r])).sum())
+        return total
+
+
+def _bf(a, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def make_workload(name, device="cuda"):
+    """(cfg, host inputs, workload) for a named config, as bench.py times it."""
+    from synth import CONFIGS, decode_inputs, layers_inputs, prefill_inputs
+    from synth.gen import LayerInputs
+    cfg = CONFIGS[name]
+    if name == "prefill":
+        p = prefill_inputs(cfg)
+        return cfg, p, PrefillWorkload(cfg, p, device)
+    if len(cfg.layers) > 1:
+        x, layers = layers_inputs(cfg)
+    else:
+        x = decode_inputs(cfg)
+        layers = [LayerInputs("F", x.q, x.q_idx, x.w, x.swa, x.planted)]
+    return cfg, (x, layers), DecodeWorkload(cfg, x, layers, device)
+
+
+# ---------------------------------------------------------------------------
 
 
 def main():
@@ -61,48 +235,21 @@ def main():
         sys.exit(2)
 
     import torch
-    from sparse_attention_fp4_csa2_amd import _lib, modes
-    from synth import CONFIGS, decode_inputs
-
+    from sparse_attention_fp4_csa2_amd import _lib
     _lib.load()
-    cfg = CONFIGS[args.config]
-    if cfg.Q != 1 or cfg.layers != "F":
-        sys.exit(f"bench.py times single-layer decode workloads; {cfg.name} is not one")
-    dev = "cuda"
     t0 = time.time()
-    x = decode_inputs(cfg)
+    cfg, host_in, wl = make_workload(args.config)
     gen_s = time.time() - t0
-
-    def bf(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    B, H, K, W, N = cfg.B, cfg.H, cfg.K, cfg.W, cfg.N
-    cap = cfg.cap
-    cache = modes.LatentCache.empty(B, cap, dev, with_groups=bool(cfg.top_groups))
-    cache.append(bf(x.latent), bf(x.keys))
-    q, q_idx, w = bf(x.q), bf(x.q_idx), torch.from_numpy(x.w).to(dev)
-    swa, swa_len = bf(x.swa), torch.from_numpy(x.swa_len).to(dev)
-    buf = modes.LayerBuffers(B, 1, H, cap, K, W, top_groups=cfg.top_groups, device=dev)
-    # decode append: one new entry per sequence, written at the last held position
-    new_lat = bf(x.latent[:, N - 1:N])
-    new_key = bf(x.keys[:, N - 1:N])
-    start = torch.full((B,), N - 1, dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
+    stream = wl.stream
     torch.cuda.synchronize()
 
-    def step():
-        _lib.append_fp4(new_lat, start, cache.records, idx_key=new_key, key_cache=cache.keys,
-                        group_sum=None, stream=stream)
-        modes.index(buf, cache, q_idx, w, stream=stream)
-        modes.attend(buf, cache, q, swa, swa_len, stream=stream)
-
     for _ in range(args.warmup):
-        step()
+        wl.step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
-        step()
+        wl.step()
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
@@ -120,39 +267,33 @@ def main():
         return a.elapsed_time(b) / reps
 
     reps = max(args.steps, 10)
-    t_index = timed(lambda: modes.index(buf, cache, q_idx, w, stream=stream), reps)
-    t_attn = timed(lambda: _lib.sparse_attn(q, cache.records, buf.idx, buf.count, cache.n_entries,
-                                            modes.SCALE, buf.o, buf.lse, ws=buf.ws_attn,
-                                            stream=stream), reps)
-    t_swa = timed(lambda: _lib.swa_merge(q, swa, swa_len, W, modes.SCALE, buf.o, buf.lse, buf.out,
-                                         buf.lse_out, buf.ws_swa, stream=stream), reps)
-    t_append = timed(lambda: _lib.append_fp4(new_lat, start, cache.records, idx_key=new_key,
-                                             key_cache=cache.keys, stream=stream), reps)
-
-    counts = buf.count.cpu().numpy()
-    n_sel_entries = int(counts.sum()) * 8
-    flops_attn = 4.0 * H * n_sel_entries * 512
+    breakdown, per_step = {}, {}
+    for name, (fn, n) in wl.calls().items():
+        breakdown[name] = timed(fn, reps)
+        per_step[name] = n
+    t_attn = breakdown["sparse_attn"]
+    wl.step()
+    torch.cuda.synchronize()
+    n_ent = wl.attended_entries()
+    flops_attn = 4.0 * cfg.H * n_ent * 512
     attn_tflops = flops_attn / (t_attn * 1e-3) / 1e12
-    kv_bytes = n_sel_entries * 272
-    kv_tbps = kv_bytes / (t_attn * 1e-3) / 1e12
-    idx_bytes = B * N * 128
-    idx_gbps = idx_bytes / (t_index * 1e-3) / 1e9
+    kv_tbps = n_ent * 272 / (t_attn * 1e-3) / 1e12
 
     if args.copy_bytes > 0:
         n = args.copy_bytes // 4
-        src = torch.randn(n, device=dev)
+        src = torch.randn(n, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
-    traffic = stored_traffic()
-
+    rows = wl.rows
+    prefill = args.config == "prefill"
     result = {
         "metric": METRIC,
-        "value": round(B / (ms_step * 1e-3), 1),
-        "unit": "queries/s",
+        "value": round(rows / (ms_step * 1e-3), 1),
+        "unit": "tokens/s" if prefill else "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -162,59 +303,134 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic (seeded N(0,1) bf16, planted relevant blocks)",
-        "config": {"workload": f"{cfg.name}: decode, B {B}, H {H}, {N} MXFP4 entries/seq "
-                               f"({N // 8} blocks of 8), indexer {cfg.Hi}x64, top-K {K}, window {W}",
-                   "global_batch": B, "seq_len": 2 * N, "parallelism": "single GPU"},
+        "config": workload_config(cfg, rows),
         "fp4_kv_read_TBps": round(kv_tbps, 3),
-        "breakdown_ms": {"append": round(t_append, 4), "index_topk": round(t_index, 4),
-                         "sparse_attn": round(t_attn, 4), "swa_merge": round(t_swa, 4)},
-        "indexer_GBps": round(idx_gbps, 1),
+        "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
+        "launches_per_step": per_step,
         "compute": "MXFP4 cache dequantised to fp16 for fp16 MFMA, fp32 accumulate; window in bf16",
         "roofline": {"kernel": "csa2_sparse_attn (attention + split-K combine)", "bound": "mfma",
-                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_FP16_TFLOPS, 4),
+                     "traffic": stored_traffic(args.config),
                      "flops_per_launch": flops_attn},
         "setup_s": round(gen_s, 1),
     }
+    if not prefill:
+        idx_bytes = wl.B * cfg.N * 128 if not cfg.top_groups else \
+            wl.B * (cfg.cap // 512 * 256 + cfg.top_groups * 512 * 128)
+        result["indexer_GBps"] = round(idx_bytes / (breakdown["index_topk"] * 1e-3) / 1e9, 1)
+    if len(cfg.layers) > 1:
+        result["reuse_saving_ms"] = round(breakdown["index_topk"] * cfg.layers.count("U"), 4)
 
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(cfg, host_in, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
-def stored_traffic():
+def workload_config(cfg, rows):
+    if cfg.name == "prefill":
+        desc = (f"prefill: {cfg.Q} query tokens after {cfg.prior} cached entries (+{cfg.Q // 2} "
+                f"appended), H {cfg.H}, indexer {cfg.Hi}x64, top-K {cfg.K} per row, window {cfg.W}, causal")
+    else:
+        desc = (f"{cfg.name}: decode, B {cfg.B}, H {cfg.H}, {cfg.N} MXFP4 entries/seq "
+                f"({cfg.N // 8} blocks of 8), indexer {cfg.Hi}x64"
+                + (f" two-level ({cfg.top_groups} of {cfg.cap // 512} groups)" if cfg.top_groups else "")
+                + f", top-K {cfg.K}, window {cfg.W}"
+                + (f", layers {'/'.join(cfg.layers)}" if len(cfg.layers) > 1 else ""))
+    return {"workload": desc, "global_batch": rows, "seq_len": 2 * cfg.N, "parallelism": "single GPU"}
+
+
+def stored_traffic(config):
     """Measured HBM bytes per csa2_sparse_attn call, or None once the kernel source changed."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(config)
+    if not os.path.exists(path):
         return None
-    rec = json.load(open(TRAFFIC_FILE))
+    rec = json.load(open(path))
     digest = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
     if rec.get("attention_hip_sha256") != digest:
         return None
     return rec.get("bytes_per_call")
 
 
-def cpu_baseline(cfg, x, budget_s):
-    """Time the fp64 oracle on a bounded sample of decode rows (whole step per row)."""
-    from oracle import modes as omodes, mxfp4
+# ---------------------------------------------------------------------------
+# oracle baseline
+
+
+def _oracle_records(latent_seq, blocks, nb):
+    """Record cache holding only the given blocks (built through the oracle's encoder)."""
+    from oracle import mxfp4
+    cache = np.zeros((nb, RECORD), dtype=np.uint8)
+    n = latent_seq.shape[0]
+    for b in np.asarray(blocks, dtype=np.int64):
+        if 0 <= b < nb:
+            lo, hi = 8 * int(b), min(8 * int(b) + 8, n)
+            if hi > lo:
+                mxfp4.write_records(cache, latent_seq[lo:hi], lo)
+    return cache
+
+
+def cpu_baseline(cfg, host_in, budget_s):
+    """Time the fp64 oracle on a bounded sample of rows (whole step per row).
+
+    Timed: indexer + top-K (Full / Reindex layers) and attention + window +
+    merge for every layer.  Not timed: building the record bytes of the
+    selected blocks, which stand for cache contents written at append time.
+    """
+    from oracle import modes as om
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = 1
+    nb = cfg.cap // 8
     done, elapsed = 0, 0.0
-    for b in range(cfg.B):
-        rec = mxfp4.build_records(x.latent[b], cfg.cap)       # cache contents (not timed)
-        t = time.perf_counter()
-        omodes.full_layer(x.q[b, 0], x.q_idx[b, 0], x.w[b, 0], x.keys[b], rec, cfg.N, cfg.K,
-                          x.swa[b], int(x.swa_len[b]), cfg.W, top_groups=cfg.top_groups or None)
-        elapsed += time.perf_counter() - t
-        done += 1
-        if elapsed >= budget_s:
-            break
-    return {"value": round(done / elapsed, 3), "unit": "queries/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} of {cfg.B} rows of {cfg.name} (index + top-K + attention + window merge "
-                      f"per row, fp64 NumPy), {elapsed:.1f} s"}
+    if cfg.name == "prefill":
+        p = host_in
+        Q = p["q"].shape[1]
+        N = int(p["n_entries"][0])
+        order = np.random.default_rng(0).permutation(Q)
+        for r in order:
+            t = time.perf_counter()
+            idx, cnt = om.select_blocks(p["q_idx"][0, r], p["w"][0, r], p["keys"][0], N, cfg.K,
+                                        q_pos=int(p["q_pos"][0, r]), n_blocks=nb)
+            elapsed += time.perf_counter() - t
+            rec = _oracle_records(p["latent"][0], idx[:cnt], nb)
+            t = time.perf_counter()
+            om.attend_row(p["q"][0, r], rec, idx, cnt, N, p["swa"][0], int(p["swa_len"][0]), cfg.W,
+                          q_pos=int(p["q_pos"][0, r]), swa_pos0=int(p["swa_pos0"][0]))
+            elapsed += time.perf_counter() - t
+            done += 1
+            if elapsed >= budget_s:
+                break
+        unit, total = "tokens/s", Q
+        what = "index + top-K + attention + window merge per query token, causal"
+    else:
+        x, layers = host_in
+        total = x.latent.shape[0]
+        for b in range(total):
+            prev = None
+            for L in layers:
+                if L.mode in ("F", "R"):
+                    t = time.perf_counter()
+                    idx, cnt = om.select_blocks(L.q_idx[b, 0], L.w[b, 0], x.keys[b], int(x.n_entries[b]),
+                                                cfg.K, top_groups=cfg.top_groups or None, n_blocks=nb)
+                    elapsed += time.perf_counter() - t
+                else:
+                    idx, cnt = prev
+                rec = _oracle_records(x.latent[b], idx[:cnt], nb)
+                t = time.perf_counter()
+                om.attend_row(L.q[b, 0], rec, idx, cnt, int(x.n_entries[b]), L.swa[b], int(x.swa_len[b]),
+                              cfg.W)
+                elapsed += time.perf_counter() - t
+                prev = (idx, cnt)
+            done += 1
+            if elapsed >= budget_s:
+                break
+        unit = "queries/s"
+        what = (f"index + top-K + attention + window merge per row, {len(layers)} layer(s) "
+                f"{''.join(L.mode for L in layers)}")
+    return {"value": round(done / elapsed, 3), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {total} rows of {cfg.name} ({what}; fp64 NumPy), {elapsed:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -9,6 +9,8 @@ the planted scores just above the best unplanted block, using a scoring
 function supplied by the caller.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -16,7 +18,7 @@ import numpy as np
 __all__ = [
     "rng_for", "bf16_rne", "bf16_to_f32", "normal_bf16", "DecodeInputs",
     "decode_inputs", "choose_blocks", "plant_dominant", "plant_tight",
-    "plant_groups", "layer_query", "prefill_inputs",
+    "plant_groups", "layer_query", "prefill_inputs", "LayerInputs", "layers_inputs",
 ]
 
 D = 512
@@ -38,12 +40,30 @@ def bf16_to_f32(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def normal_bf16(rng, shape, chunk=1 << 24):
-    """N(0,1) float32 draws rounded to bfloat16, drawn in chunks to bound memory."""
-    out = np.empty(int(np.prod(shape)), dtype=np.uint16)
-    for s in range(0, out.size, chunk):
-        e = min(out.size, s + chunk)
-        out[s:e] = bf16_rne(rng.standard_normal(e - s, dtype=np.float32))
+def normal_bf16(rng, shape, chunk=1 << 22):
+    """N(0,1) float32 draws rounded to bfloat16.
+
+    Chunk i of ``chunk`` values is drawn from its own PCG64 stream, seeded by
+    the i-th 63-bit integer drawn from ``rng``; chunks are filled by a thread
+    pool (the draws are the same for any number of threads).
+    """
+    size = int(np.prod(shape))
+    out = np.empty(size, dtype=np.uint16)
+    n_chunks = max(1, (size + chunk - 1) // chunk)
+    seeds = rng.integers(0, 2 ** 63 - 1, size=n_chunks, dtype=np.int64)
+
+    def fill(i):
+        s, e = i * chunk, min(size, (i + 1) * chunk)
+        if e > s:
+            g = np.random.Generator(np.random.PCG64(int(seeds[i])))
+            out[s:e] = bf16_rne(g.standard_normal(e - s, dtype=np.float32))
+
+    if n_chunks == 1:
+        fill(0)
+    else:
+        workers = max(1, min(8, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, range(n_chunks)))
     return out.reshape(shape)
 
 
@@ -233,3 +253,50 @@ def prefill_inputs(cfg, seed=None, q_rows=None, n_dirs=4, c=3.0, beta=1.0):
                 swa=swa, swa_len=np.array([swa_total], np.int32),
                 swa_pos0=np.array([swa_pos0], np.int32), prior=prior,
                 n_entries=np.array([N], np.int32), planted=planted)
+
+
+@dataclass
+class LayerInputs:
+    mode: str               # "F" Full, "R" Reindex, "U" Reuse
+    q: np.ndarray           # u16 [B][Q][H][512]  the layer's own attention query
+    q_idx: np.ndarray       # u16 [B][Q][Hi][64]  own indexer query (F, R), else None
+    w: np.ndarray           # f32 [B][Q][Hi]      own indexer weights (F, R), else None
+    swa: np.ndarray         # u16 [B][W][512]     own sliding window
+    planted: list = field(default_factory=list)
+
+
+def layers_inputs(cfg, seed=None, c=3.0):
+    """Shared cache + one LayerInputs per letter of ``cfg.layers`` (e.g. "FRUU").
+
+    The first layer uses the decode_inputs draw (its plant included).  Every
+    later layer draws its own query and window; a Reindex layer also draws its
+    own indexer query and plants its own K blocks (one key c * q_h* each, blocks
+    disjoint from the earlier plants) into the shared keys.
+    """
+    base = cfg.seed if seed is None else seed
+    x = decode_inputs(cfg, seed=base, c=c)
+    rng = rng_for(base + 7919)
+    layers = []
+    used = [np.asarray(p) for p in x.planted]
+    for i, mode in enumerate(cfg.layers):
+        if i == 0:
+            if mode != "F":
+                raise ValueError("the first layer must be Full")
+            layers.append(LayerInputs("F", x.q, x.q_idx, x.w, x.swa, x.planted))
+            continue
+        q, q_idx, w = layer_query(rng, x.q.shape[0], cfg.Q, cfg.H, cfg.Hi)
+        swa = normal_bf16(rng, (x.q.shape[0], cfg.W, D))
+        planted = []
+        if mode == "R":
+            for b in range(x.q.shape[0]):
+                nbp = (int(x.n_entries[b]) + 7) // 8
+                blocks = choose_blocks(rng, nbp, cfg.K, exclude=used[b])
+                plant_dominant(x.keys[b], x.n_entries[b], q_idx[b, 0], w[b, 0], blocks, rng, c=c)
+                used[b] = np.concatenate([used[b], blocks])
+                planted.append(blocks)
+            layers.append(LayerInputs("R", q, q_idx, w, swa, planted))
+        elif mode == "U":
+            layers.append(LayerInputs("U", q, None, None, swa, []))
+        else:
+            raise ValueError(mode)
+    return x, layers
