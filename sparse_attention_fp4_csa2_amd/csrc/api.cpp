@@ -142,7 +142,7 @@ int csa2_topk(const float* scores, int rows, int n, int k, int32_t* idx, int32_t
 size_t csa2_sparse_attn_ws(int B, int Q, int H, int top_k) {
   if (B <= 0 || Q <= 0 || H <= 0 || top_k <= 0) return 0;
   const int rows = B * Q;
-  const int s = attn_splits(rows, H, attn_n_tiles(top_k));
+  const int s = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
   if (s <= 1) return 0;
   return align_up((size_t)rows * s * H * CSA2_D * sizeof(float)) +
          align_up((size_t)rows * s * H * sizeof(float));
@@ -157,8 +157,9 @@ int csa2_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx
   if (cap % CSA2_BLOCK != 0 || !(scale > 0.f) || !isfinite(scale)) return CSA2_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(o, 16)) return CSA2_ERR_INVALID_ARG;
   if (H > CSA2_MAX_HEADS) return CSA2_ERR_UNSUPPORTED;
+  if ((size_t)cap / CSA2_BLOCK * CSA2_RECORD_BYTES > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
   const int rows = B * Q;
-  const int splits = attn_splits(rows, H, attn_n_tiles(top_k));
+  const int splits = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
   const size_t need = csa2_sparse_attn_ws(B, Q, H, top_k);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WS_TOO_SMALL;
   if (need > 0 && !aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
@@ -170,13 +171,13 @@ int csa2_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx
   hipStream_t st = as_stream(stream);
   if (splits == 1) {
     p.o_out = o; p.lse_out = lse;
-    return launch_status(launch_attention(p, true, st));
+    return launch_status(launch_sparse_fp4(p, st));
   }
   float* o_part = static_cast<float*>(ws);
   float* lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                              align_up((size_t)rows * splits * H * CSA2_D * sizeof(float)));
   p.o_out = o_part; p.lse_out = lse_part;
-  int rc = launch_attention(p, true, st);
+  int rc = launch_sparse_fp4(p, st);
   if (!rc) rc = launch_combine(o_part, lse_part, rows, splits, H, nullptr, nullptr, o, lse, st);
   return launch_status(rc);
 }

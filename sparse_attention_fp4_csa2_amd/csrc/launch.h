@@ -50,6 +50,9 @@ struct AttnParams {
 };
 
 int attn_splits(int rows, int H, int n_tiles);
+// MXFP4 source: 32-head workgroups, two per CU (sparse_fp4.hip)
+int sparse_fp4_splits(int rows, int H, int n_tiles);
+int launch_sparse_fp4(const AttnParams& p, hipStream_t stream);
 int launch_attention(const AttnParams& p, bool fp4_source, hipStream_t stream);
 
 // Merge split partials (and an optional extra branch) -> out [rows][H][512], lse [rows][H].

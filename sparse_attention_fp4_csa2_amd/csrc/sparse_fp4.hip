@@ -1,0 +1,473 @@
+// Split-K multi-head attention over the selected blocks of the MXFP4 latent
+// cache (gather + dequant + Q.K + online softmax + P.V in one pass).
+//
+// What is computed: one 512-d latent per entry is the key AND the value of
+// every head (paper-digest.app page, Core Mechanics, "Compressed along three
+// axes"); only the top-K selected blocks of 8 entries are attended
+// (observer.broadside.tech card, Key ideas, "CSA2 with three static layer
+// modes").  Per head: z_j = scale * q . V_j, o = softmax(z) V, lse = log sum
+// exp z, over the selected, present, visible entries; splits of the selection
+// are merged by log-sum-exp afterwards.
+//
+// Organisation: one workgroup = (row, split, group of 32 heads), 4 waves; wave
+// dq owns latent dims [128dq, 128dq + 128) for all 32 heads.  Two workgroups
+// fit on a CU (<= 256 registers per lane, ~71 KB LDS), so one wave's VALU work
+// overlaps the other's MFMAs.  A tile is 32 entries (4 blocks).  Per tile:
+//  * Q.K: lane (entry e = lane%32, half hh) loads 32 bytes of e's FP4 codes for
+//    the wave's dims and feeds them unconverted to v_mfma_scale_f32_32x32x64_
+//    f8f6f4 (A = E2M1 codes with their E8M0 scales, B = the query split into
+//    exact fp8 hi + lo parts): S^T[32 entries][32 heads] over 128 dims.
+//  * the 4 partial S^T tiles meet in LDS; wave dq sums the quarter of the tile
+//    it owns (entries 8dq..8dq+7), runs the online softmax on it and writes its
+//    quarter of P (fp16) back: every wave then reads the whole P^T tile as the
+//    B operand of O^T += V^T P^T (v_mfma_f32_32x32x16_f16).
+//  * V: the same codes, dequantised with v_cvt_scalef32_pk_f16_fp4 to fp16
+//    relative to a per-wave power-of-two base, go to the wave's own LDS tile
+//    (entry-major) and come back transposed with ds_read_b64_tr_b16.
+//  * the running max moves lazily (only when a head's max grows by > 2^8); a
+//    tile that needs a move takes a rare uniform slow path.
+//  * workgroup order: the head groups of one (row, split) get linear ids 8
+//    apart, i.e. the same XCD, so their shared record reads meet in one L2.
+#include "device.h"
+#include "launch.h"
+
+namespace csa2 {
+
+namespace {
+
+constexpr int TILE = 32;                 // entries per tile
+constexpr int VROWU = 20;                // 16-byte units per V row: 16 data + 4 pad
+// unit u of V row r sits at u ^ ((r >> 1) & 3): with 20-unit rows both the
+// row writes (b128) and the transposed reads are free of LDS bank conflicts
+constexpr int PROW = 40;                 // fp16 slots per P row (32 entries + 8 pad)
+constexpr int MAX_SPLIT_BLOCKS = 2048;   // selected block ids one workgroup stages in LDS
+constexpr float LAZY_LOG2 = 8.0f;        // move the running max only when it grows by > 2^8
+constexpr float M_INIT = -1.0e30f;       // finite "no max yet": exp2(x - M_INIT) never NaN
+constexpr int VBIAS = 140;               // V' = V * 2^(VBIAS - vbase): code 6 at vbase -> 6*2^13
+constexpr int QLO_SHIFT = 4;             // fp8 lo part of a query carries 2^4 more resolution
+
+typedef int int32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+struct Lds {
+  floatx4 sp[4][4][64];            // [wave][quarter][lane] partial S^T          16 KB
+  uint4 v[4][TILE * VROWU];        // [wave][entry * VROWU + unit] fp16 V tile  40 KB
+  uint16_t pb[2][32 * PROW];       // [buffer][head * PROW + slot] fp16 P        5 KB
+  float qmax[2][4][32];            // [buffer][wave][head] quarter max of z*log2e
+  int flag[2][4];                  // [buffer][wave] quarter needs a max move
+  float lsum[4][32];               // epilogue: per-wave softmax denominators
+  int32_t blk[MAX_SPLIT_BLOCKS];   // this split's selected block ids           8 KB
+};
+
+__device__ __forceinline__ floatx16 mfma_fp4_fp8(uint4 a, const int32x8& b, floatx16 c,
+                                                 uint32_t sa, uint32_t sb) {
+  const int32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, b, c, 4, 0, 0, (int)sa, 0, (int)sb);
+}
+
+__device__ __forceinline__ floatx16 mfma_f16(uint4 a, uint4 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a),
+                                                __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+}
+
+// 8 MXFP4 codes -> 8 fp16 values, times the float whose bits are scale_bits.
+__device__ __forceinline__ uint4 dequant8_f16(uint32_t codes, uint32_t scale_bits) {
+  const float sc = __uint_as_float(scale_bits);
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 3));
+  return r;
+}
+
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {    // v_cvt_pk_f16_f32, RNE
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, halfx2));
+}
+
+// fp8 E4M3 (OCP) byte -> float, for the hi/lo query split
+__device__ __forceinline__ float fp8_byte_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15, m = b & 7;
+  const float v = e ? ldexpf(1.f + (float)m * 0.125f, (int)e - 7) : ldexpf((float)m * 0.125f, -6);
+  return (b & 0x80) ? -v : v;
+}
+
+// (lane l, lane l^32) reductions: v_permlane32_swap gives {lane l%32, lane l%32 + 32}
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = max(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+struct Raw {
+  uint4 c0, c1;    // 32 bytes of codes: this wave's dims 64s + 32hh + [0, 32), s = 0, 1
+  uint32_t sc;     // scale bytes of groups 4dq .. 4dq + 3
+  int valid;
+};
+
+constexpr int BUF_DWORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
+
+}  // namespace
+
+__global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_units, int hgroups) {
+  __shared__ Lds lds;
+  // ---- workgroup -> (row, split, head group), XCD-aware ------------------
+  const int L = blockIdx.x;
+  const int unit = (L / (8 * hgroups)) * 8 + (L & 7);
+  const int hgi = (L >> 3) % hgroups;
+  if (unit >= n_units) return;
+  const int row = unit / p.splits;
+  const int split = unit - row * p.splits;
+
+  const int tid = threadIdx.x;
+  const int dq = tid >> 6;        // wave: latent dims [128dq, 128dq + 128)
+  const int lane = tid & 63;
+  const int e = lane & 31;        // Q.K: entry of the tile;  S^T, P^T, O^T: head of the group
+  const int hh = lane >> 5;
+  const int b = row / p.Q;
+  const int head = 32 * hgi + e;
+  const bool head_ok = head < p.H;
+
+  int n_items = p.count[row];
+  n_items = n_items < 0 ? 0 : (n_items > p.top_k ? p.top_k : n_items);
+  const int t_pos = p.q_pos ? p.q_pos[row] : 0;
+  const int n_tiles = (n_items + 3) / 4;
+  const int tps = (n_tiles + p.splits - 1) / p.splits;
+  const int t_begin = split * tps;
+  const int t_end = min(n_tiles, t_begin + tps);
+  const int n_ent = p.n_entries[b];
+  const int nb_cap = p.cap / BLOCK;
+  // entries below lim are present and visible (entry j covers raw positions
+  // 2j and 2j + 1; a causal query at raw position t sees 2j + 1 <= t)
+  const int lim = p.q_pos ? min(n_ent, (t_pos + 1) >> 1) : n_ent;
+  const int n_items_split = min(n_items, 4 * t_end);
+  // this sequence's records as a raw buffer: ids outside [0, nb_cap) (the -1
+  // padding included) fall outside it and load zeros
+  const __amdgpu_buffer_rsrc_t rec_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.cache + (size_t)b * nb_cap * RECORD), (short)0, nb_cap * RECORD, BUF_DWORD3);
+  const uint32_t code_off = (e & 7) * 256 + 64 * dq + 16 * hh;
+  const uint32_t sc_off = SCALE_OFF + (e & 7) * 16 + 4 * dq;
+  const float c_log2 = p.scale_log2;
+
+  // ---- query: exact fp8 hi + lo B operands ------------------------------
+  // lane (head, hh), k-step s, byte i: dim 128dq + 64s + 32(i/16) + 16hh + i%16
+  int32x8 qhi[2], qlo[2];
+  uint32_t qsb_hi, qsb_lo;
+  {
+    const uint16_t* qrow = p.q + ((size_t)row * p.H + head) * D + 128 * dq + 16 * hh;
+    float qv[2][32];
+    float mx = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint4* src = reinterpret_cast<const uint4*>(qrow + 64 * s + 32 * half);
+        const uint4 u0 = head_ok ? src[0] : make_uint4(0, 0, 0, 0);
+        const uint4 u1 = head_ok ? src[1] : make_uint4(0, 0, 0, 0);
+        const uint32_t wv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float a = __uint_as_float(wv[k] << 16);
+          const float c = __uint_as_float(wv[k] & 0xFFFF0000u);
+          qv[s][16 * half + 2 * k] = a;
+          qv[s][16 * half + 2 * k + 1] = c;
+          mx = fmaxf(mx, fmaxf(fabsf(a), fabsf(c)));
+        }
+      }
+    }
+    mx = pair_max(mx);
+    int cq = 0;
+    if (mx > 0.f && mx < __builtin_inff()) cq = 7 - ilogbf(mx);
+    const float f = ldexpf(1.f, cq), flo = ldexpf(1.f, QLO_SHIFT);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        int hw = 0, lw = 0;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float a0 = qv[s][4 * d + 2 * k] * f, a1 = qv[s][4 * d + 2 * k + 1] * f;
+          const int h2 = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+          const float h0 = fp8_byte_to_f32((uint32_t)h2 & 0xFF);
+          const float h1 = fp8_byte_to_f32(((uint32_t)h2 >> 8) & 0xFF);
+          const int l2 = __builtin_amdgcn_cvt_pk_fp8_f32((a0 - h0) * flo, (a1 - h1) * flo, 0, false);
+          hw |= (h2 & 0xFFFF) << (16 * k);
+          lw |= (l2 & 0xFFFF) << (16 * k);
+        }
+        qhi[s][d] = hw;
+        qlo[s][d] = lw;
+      }
+    }
+    qsb_hi = (uint32_t)(127 - cq);
+    qsb_lo = (uint32_t)(127 - cq - QLO_SHIFT);
+  }
+
+  {
+    const int i0 = 4 * t_begin, i1 = min(4 * t_end, n_items);
+    for (int i = i0 + tid; i < i1; i += 256) lds.blk[i - i0] = p.idx[(size_t)row * p.top_k + i];
+  }
+  __syncthreads();
+
+  // ---- tile helpers -----------------------------------------------------
+  auto fetch = [&](int t, Raw& r) {
+    const int item = 4 * t + (e >> 3);
+    const int blk = item < n_items_split ? lds.blk[min(item - 4 * t_begin, MAX_SPLIT_BLOCKS - 1)] : -1;
+    r.valid = (uint32_t)blk < (uint32_t)nb_cap && blk * BLOCK + (e & 7) < lim;
+    const uint32_t off = (uint32_t)blk * RECORD;
+    r.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rec_rsrc, off + code_off, 0, 0));
+    r.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rec_rsrc, off + code_off + 32, 0, 0));
+    r.sc = __builtin_amdgcn_raw_buffer_load_b32(rec_rsrc, off + sc_off, 0, 0);
+  };
+  // largest scale byte of the wave's groups in the tile (every fetched entry,
+  // so no dequantised value can overflow fp16), folded into the running base
+  auto raise_base = [&](const Raw& r, int cur) -> int {
+    const uint32_t s = r.sc;
+    const int smax = max(max((int)(s & 0xFF), (int)((s >> 8) & 0xFF)),
+                         max((int)((s >> 16) & 0xFF), (int)(s >> 24)));
+    if (__any(smax > cur)) return max(cur, wave_max_int(smax));
+    return cur;
+  };
+  uint4* const vrow = &lds.v[dq][e * VROWU];
+  int vu[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) vu[u] = (4 * hh + u) ^ ((e >> 1) & 3);
+  // V (fp16 relative to base vb) of the lane's 64 dims: 8 fragments of 8 values
+  auto dequant_v = [&](const Raw& r, int vb, uint4 (&kf)[8]) {
+    const uint32_t s8 = r.sc >> (8 * hh);           // byte 0: group 4dq+hh, byte 2: 4dq+2+hh
+    const uint32_t b0 = (uint32_t)max((int)(s8 & 0xFF) - vb + VBIAS, 0) << 23;
+    const uint32_t b1 = (uint32_t)max((int)((s8 >> 16) & 0xFF) - vb + VBIAS, 0) << 23;
+    kf[0] = dequant8_f16(r.c0.x, b0); kf[1] = dequant8_f16(r.c0.y, b0);
+    kf[2] = dequant8_f16(r.c0.z, b0); kf[3] = dequant8_f16(r.c0.w, b0);
+    kf[4] = dequant8_f16(r.c1.x, b1); kf[5] = dequant8_f16(r.c1.y, b1);
+    kf[6] = dequant8_f16(r.c1.z, b1); kf[7] = dequant8_f16(r.c1.w, b1);
+  };
+  // ... into row e of the wave's V tile: units 8s + 4hh + u (u < 4), swizzled
+  auto write_v = [&](const uint4 (&kf)[8]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { vrow[vu[u]] = kf[u]; vrow[vu[u] + 8] = kf[4 + u]; }
+  };
+  // Q.K partial S^T over the wave's 128 dims -> LDS
+  auto qk_s = [&](const Raw& r) {
+    // the MFMA reads the E8M0 scale from byte 0 of its scale operand
+    const uint32_t s8 = r.sc >> (8 * hh);
+    const uint32_t s8b = s8 >> 16;
+    floatx16 sacc = floatx16{};
+    sacc = mfma_fp4_fp8(r.c0, qhi[0], sacc, s8, qsb_hi);
+    sacc = mfma_fp4_fp8(r.c0, qlo[0], sacc, s8, qsb_lo);
+    sacc = mfma_fp4_fp8(r.c1, qhi[1], sacc, s8b, qsb_hi);
+    sacc = mfma_fp4_fp8(r.c1, qlo[1], sacc, s8b, qsb_lo);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      lds.sp[dq][j][lane] = floatx4{sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3]};
+  };
+
+  floatx16 oacc[4];       // O^T: [dims 128dq + 32mt + 8(i/4) + 4hh + i%4][head]
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) oacc[mt] = floatx16{};
+  float m_run = M_INIT;   // running max of z * log2(e), per head (lane pair)
+  float l_lane = 0.f;     // softmax denominator over this lane's quarter entries
+  int base_o = 0;         // O^T is in units of 2^(base_o - VBIAS)
+  int base_v = 0;         // base of the newest dequantised V tile
+  uint2 vt[2][4][2];      // V^T A fragments of the previous tile, [ks2][mt][half]
+  uint4 pfr[2];           // P^T B fragments of the previous tile, [ks2]
+  int base_prev = 0;      // base of those V^T fragments
+  bool have_pv = false;
+
+  // P slot of entry 8dq + 4hh + r within its 16-entry k-step, matching the
+  // k -> entry order of the transposed V^T reads: k = 8hh' + j holds entry
+  // 4hh' + j (j < 4) or 8 + 4hh' + j - 4
+  const int pslot = 16 * (dq >> 1) + 8 * hh + 4 * (dq & 1);
+
+  Raw rn;
+  uint32_t vmask_cur = 0;
+  if (t_begin < t_end) {
+    Raw r0;
+    fetch(t_begin, r0);
+    fetch(t_begin + 1, rn);
+    base_v = raise_base(r0, 0);
+    base_o = base_v;
+    uint4 kf0[8];
+    dequant_v(r0, base_v, kf0);
+    write_v(kf0);
+    qk_s(r0);
+    vmask_cur = (uint32_t)__ballot(r0.valid);
+  }
+  __syncthreads();
+
+  auto issue_pv = [&]() {
+    if (base_prev != base_o) {        // that tile's V used a higher base: rescale O exactly
+      const float f = ldexpf(1.f, base_o - base_prev);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) oacc[mt] *= f;
+      base_o = base_prev;
+    }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint4 va = make_uint4(vt[ks2][mt][0].x, vt[ks2][mt][0].y, vt[ks2][mt][1].x, vt[ks2][mt][1].y);
+        oacc[mt] = mfma_f16(va, pfr[ks2], oacc[mt]);
+      }
+  };
+
+  const int sl = lane & 15, blk16 = lane >> 4;
+  const int u0 = 2 * (blk16 & 1) + ((sl & 3) >> 1);
+  auto read_pfr = [&](int buf) {
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+      pfr[ks2] = *reinterpret_cast<const uint4*>(&lds.pb[buf][e * PROW + 16 * ks2 + 8 * hh]);
+  };
+  auto write_p = [&](int buf, const float (&pr)[4]) {
+    uint16_t* pdst = &lds.pb[buf][e * PROW + pslot];
+    *reinterpret_cast<uint2*>(pdst) = make_uint2(pack_f16(pr[0], pr[1]), pack_f16(pr[2], pr[3]));
+  };
+
+  // Pipeline, two barriers per tile t:
+  //   X(t) = [B1(t), B2(t)): P.V(t-1) MFMAs | S(t) quarter reads, softmax,
+  //          P(t) written; dequantisation of tile t+1 into registers
+  //   Y(t) = [B2(t), B1(t+1)): P^T(t), V^T(t) reads | V(t+1) written, Q.K(t+1)
+  //          MFMAs, S(t+1) partial written; records of tile t+2 requested
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = t & 1;
+    const bool more = t + 1 < t_end;
+    // ---- X(t) ---------------------------------------------------------------
+    floatx4 sw[4];
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) sw[w2] = lds.sp[w2][dq][lane];
+    if (have_pv) issue_pv();
+    uint4 kf[8];
+    int base_next = base_v;
+    if (more) {
+      base_next = raise_base(rn, base_v);
+      dequant_v(rn, base_next, kf);
+    }
+    floatx4 sq;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sq[r] = (sw[0][r] + sw[1][r]) + (sw[2][r] + sw[3][r]);
+    if (vmask_cur != 0xFFFFFFFFu) {
+      const uint32_t vq = vmask_cur >> (8 * dq + 4 * hh);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (!((vq >> r) & 1u)) sq[r] = -__builtin_inff();
+    }
+    const float hmax = pair_max(fmaxf(fmaxf(sq[0], sq[1]), fmaxf(sq[2], sq[3]))) * c_log2;
+    const bool bump = hmax > m_run + LAZY_LOG2;
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[r], c_log2, -m_run));
+    write_p(buf, pr);
+    const int any_bump = __any(bump) ? 1 : 0;
+    if (lane < 32) lds.qmax[buf][dq][lane] = hmax;
+    if (lane == 0) lds.flag[buf][dq] = any_bump;
+    __syncthreads();
+
+    // ---- Y(t): every LDS read of the tile at once: flags, P^T(t), V^T(t) ------
+    const int4 fl = *reinterpret_cast<const int4*>(&lds.flag[buf][0]);
+    read_pfr(buf);
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const int r0 = 16 * ks2 + 4 * (blk16 >> 1) + (sl >> 2);
+      const int x0 = (r0 >> 1) & 3, x1 = ((r0 + 8) >> 1) & 3;
+      const uint16_t* vb0 = reinterpret_cast<const uint16_t*>(&lds.v[dq][r0 * VROWU + (u0 ^ x0)]) + 4 * (sl & 1);
+      const uint16_t* vb1 = reinterpret_cast<const uint16_t*>(&lds.v[dq][(r0 + 8) * VROWU + (u0 ^ x1)]) + 4 * (sl & 1);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        vt[ks2][mt][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                      (lds_bf16x4*)(vb0 + 32 * mt)));
+        vt[ks2][mt][1] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                      (lds_bf16x4*)(vb1 + 32 * mt)));
+      }
+    }
+    base_prev = base_v;
+    have_pv = true;
+
+    // rare: a head's max moved by more than 2^8 (always on the first tile)
+    if (fl.x | fl.y | fl.z | fl.w) {
+      const float tmax = fmaxf(fmaxf(lds.qmax[buf][0][e], lds.qmax[buf][1][e]),
+                               fmaxf(lds.qmax[buf][2][e], lds.qmax[buf][3][e]));
+      const float m_new = tmax > m_run + LAZY_LOG2 ? tmax : m_run;
+      if (__any(m_new != m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) oacc[mt] *= alpha;
+        l_lane *= alpha;
+        m_run = m_new;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[r], c_log2, -m_run));
+      write_p(buf, pr);
+      __syncthreads();
+      read_pfr(buf);
+    }
+    l_lane += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+
+    if (more) {
+      write_v(kf);                // after this wave's V^T(t) reads: the LDS keeps their order
+      qk_s(rn);
+      vmask_cur = (uint32_t)__ballot(rn.valid);
+      base_v = base_next;
+      fetch(t + 2, rn);
+      __syncthreads();
+    }
+  }
+  if (have_pv) issue_pv();
+
+  // ---- finalize: denominators across the 4 quarter owners -----------------
+  const float lq = pair_sum(l_lane);
+  if (lane < 32) lds.lsum[dq][lane] = lq;
+  __syncthreads();
+  const float l = (lds.lsum[0][e] + lds.lsum[1][e]) + (lds.lsum[2][e] + lds.lsum[3][e]);
+  if (head_ok) {
+    const float il = l > 0.f ? 1.f / l : 0.f;
+    if (dq == 0 && hh == 0) {
+      const float lse = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
+      p.lse_out[((size_t)row * p.splits + split) * p.H + head] = lse;
+    }
+    const float f = ldexpf(il, base_o - VBIAS);
+    float* dst = p.o_out + (((size_t)row * p.splits + split) * p.H + head) * D + 128 * dq + 4 * hh;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<float4*>(dst + 32 * mt + 8 * jj) =
+            make_float4(oacc[mt][4 * jj] * f, oacc[mt][4 * jj + 1] * f, oacc[mt][4 * jj + 2] * f,
+                        oacc[mt][4 * jj + 3] * f);
+  }
+}
+
+int sparse_fp4_splits(int rows, int H, int n_tiles) {
+  const int hgroups = (H + 31) / 32;
+  const int wgs = rows * hgroups;
+  int s = (512 + wgs - 1) / wgs;                 // two workgroups per CU
+  const int cap_by_tiles = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
+  if (s > cap_by_tiles) s = cap_by_tiles;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  const int min_s = (n_tiles + MAX_SPLIT_BLOCKS / 4 - 1) / (MAX_SPLIT_BLOCKS / 4);
+  if (s < min_s) s = min_s;
+  return s;
+}
+
+int launch_sparse_fp4(const AttnParams& p, hipStream_t stream) {
+  const int hgroups = (p.H + 31) / 32;
+  const int n_units = p.rows * p.splits;
+  const int groups = (n_units + 7) / 8;
+  const long long n_wg = (long long)groups * 8 * hgroups;
+  if (n_wg > 0x7FFFFFFF) return -4;
+  sparse_fp4_kernel<<<dim3((unsigned)n_wg), 256, 0, stream>>>(p, n_units, hgroups);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace csa2
