@@ -73,6 +73,10 @@ def _index_gpu(x, cfg, n_entries, top_groups=0, q_pos=None, group_sum=None):
                    cfg.K, idx, cnt, ws, group_sum=gs, q_pos=None if q_pos is None else dev(q_pos),
                    top_groups=top_groups)
     torch.cuda.synchronize()
+    if x.get("want_scores"):
+        # flat call: the workspace starts with the fp32 block scores [rows][cap/8]
+        sc = host(ws[:B * Q * (cap // 8) * 4].view(torch.float32)).reshape(B, Q, cap // 8)
+        return host(idx), host(cnt), sc
     return host(idx), host(cnt)
 
 
@@ -154,3 +158,41 @@ def test_two_level_small_bit_exact_and_all_groups_equals_flat():
     got_all, cnt_all = _index_gpu(d, cfg, ne, top_groups=32)
     got_flat, cnt_flat = _index_gpu(d, cfg, ne)
     assert np.array_equal(got_all, got_flat) and np.array_equal(cnt_all, cnt_flat)
+
+
+@pytest.mark.parametrize("hi", [8, 5])
+def test_many_rows_per_sequence_scores_and_selection(hi):
+    # 40 causal query rows per sequence (two full 16-row tiles and a ragged one),
+    # the multi-row MFMA indexer; block scores compared value by value
+    B, Q, cap, K = 2, 40, 4096 + 512, 64
+    cfg = Config("m", B=B, Q=Q, H=16, N=cap, Hi=hi, K=K, W=16, seed=21)
+    rng = rng_for(21 + hi)
+    keys = normal_bf16(rng, (B, cap, 64))
+    q_idx = normal_bf16(rng, (B, Q, hi, 64))
+    w = rng.standard_normal((B, Q, hi)).astype(np.float32)
+    ne = np.array([cap, 3001], np.int32)
+    q_pos = np.sort(rng.integers(0, 2 * cap + 64, size=(B, Q)), axis=1).astype(np.int32)
+    q_pos[0, 0], q_pos[1, -1] = 0, 2 * cap + 63           # nothing visible / everything visible
+    got, cnt, sc = _index_gpu(dict(q_idx=q_idx, w=w, keys=keys, cap=cap, want_scores=True), cfg, ne,
+                              q_pos=q_pos)
+    worst = 0.0
+    for b in range(B):
+        for r in range(Q):
+            s = indexer.block_scores(q_idx[b, r], w[b, r], keys[b], int(ne[b]), q_pos=int(q_pos[b, r]),
+                                     n_blocks=cap // 8)
+            fin = np.isfinite(s)
+            assert np.array_equal(np.isfinite(sc[b, r]), fin), (b, r)
+            if fin.any():
+                scale = max(1.0, np.abs(s[fin]).max())
+                worst = max(worst, np.abs(sc[b, r][fin] - s[fin]).max() / scale)
+            exp, c = topk.select(s, K)
+            assert cnt[b, r] == c, (b, r)
+            if topk.gap_at_rank(s, K) >= 1e-2:
+                assert np.array_equal(got[b, r], exp), (b, r)
+            elif c:
+                sel = got[b, r, :c]
+                uns = np.setdiff1d(np.nonzero(fin)[0], sel)
+                if uns.size:
+                    assert s[sel].min() >= s[uns].max() - 1e-4 * np.abs(s[fin]).max()
+    print(f"[parity] multi-row block scores: max|err|/max|s| = {worst:.2e}")
+    assert worst < 1e-5
