@@ -2,9 +2,10 @@
 
 One step = the whole hot path over one batch of synthetic input:
   decode    csa2_append_fp4 (one new entry per sequence) -> per layer:
-            csa2_index_topk (Full / Reindex) -> csa2_sparse_attn -> csa2_swa_merge
+            csa2_index_topk (Full / Reindex) -> csa2_attend_layer (sparse branch +
+            sliding window, merged by one log-sum-exp combine)
   prefill   csa2_append_fp4 (the chunk's 2048 entries) -> csa2_index_topk (causal,
-            every query row) -> csa2_sparse_attn -> csa2_swa_merge (causal window)
+            every query row) -> csa2_attend_layer (causal window)
 Default workload (--config decode64k): decode at 64K context, 32 sequences, 64
 heads, 32768 MXFP4 entries = 4096 blocks of 8 per sequence, 8 x 64 indexer,
 top-K 2048, window 512; seeded N(0,1) bf16 inputs with planted relevant blocks.
@@ -38,7 +39,8 @@ PEAK_HBM_GBPS = 8000.0
 RECORD = 2176
 # HBM bytes per csa2_sparse_attn call from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # counter runs, with the hash of the kernel source they were taken on
-KERNEL_SRC = os.path.join(ROOT, "sparse_attention_fp4_csa2_amd", "csrc", "attention.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "sparse_attention_fp4_csa2_amd", "csrc", f)
+               for f in ("sparse_fp4.hip", "attention.hip")]
 
 
 def traffic_file(config):
@@ -114,10 +116,13 @@ class DecodeWorkload:
         return {
             "append": (self.append, 1),
             "index_topk": (lambda: m.index(buf, self.cache, L0["q_idx"], L0["w"], stream=s), n_index),
-            "sparse_attn": (self.sparse_attn_call, len(self.layers)),
+            "attend_layer": (lambda: m.attend(buf, self.cache, L0["q"], L0["swa"], self.swa_len, stream=s),
+                             len(self.layers)),
+            # the two branches as separate calls (not part of the step; sparse_attn is the roofline unit)
+            "sparse_attn": (self.sparse_attn_call, 0),
             "swa_merge": (lambda: lib.swa_merge(L0["q"], L0["swa"], self.swa_len, self.cfg.W, m.SCALE,
                                                 buf.o, buf.lse, buf.out, buf.lse_out, buf.ws_swa,
-                                                stream=s), len(self.layers)),
+                                                stream=s), 0),
         }
 
     def sparse_attn_call(self):
@@ -178,15 +183,19 @@ class PrefillWorkload:
                             b.out, b.lse_out, b.ws_swa, swa_pos0=self.swa_pos0, q_pos=self.q_pos,
                             stream=self.stream)
 
+    def attend_call(self):
+        self.modes.attend(self.buf, self.cache, self.q, self.swa, self.swa_len, swa_pos0=self.swa_pos0,
+                          q_pos=self.q_pos, stream=self.stream)
+
     def step(self):
         self.append()
         self.index()
-        self.sparse_attn_call()
-        self.swa_call()
+        self.attend_call()
 
     def calls(self):
         return {"append": (self.append, 1), "index_topk": (self.index, 1),
-                "sparse_attn": (self.sparse_attn_call, 1), "swa_merge": (self.swa_call, 1)}
+                "attend_layer": (self.attend_call, 1),
+                "sparse_attn": (self.sparse_attn_call, 0), "swa_merge": (self.swa_call, 0)}
 
     def attended_entries(self):
         """Visible entries of the selected blocks summed over rows (causal masking counted)."""
@@ -340,14 +349,22 @@ def workload_config(cfg, rows):
     return {"workload": desc, "global_batch": rows, "seq_len": 2 * cfg.N, "parallelism": "single GPU"}
 
 
+def kernel_digest():
+    """SHA-256 over the sources of the csa2_sparse_attn kernels (attention + combine)."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def stored_traffic(config):
     """Measured HBM bytes per csa2_sparse_attn call, or None once the kernel source changed."""
     path = traffic_file(config)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    digest = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if rec.get("attention_hip_sha256") != digest:
+    digest = kernel_digest()
+    if rec.get("kernel_sources_sha256") != digest:
         return None
     return rec.get("bytes_per_call")
 

@@ -110,8 +110,9 @@ int csa2_topk(const float* scores, int rows, int n, int k, int32_t* idx, int32_t
  * For each row r = (b, q) and head h: z_j = scale * (q_h . V_j) over the
  * present, visible entries j of the blocks idx[r][0..count[r]); V_j = the
  * dequantised entry; o = softmax(z) V (fp32), lse = log sum exp z.  An empty
- * selection gives o = 0, lse = -inf.  bf16 MFMA with fp32 accumulation; the
- * softmax weights are rounded to bf16 before the value product.
+ * selection gives o = 0, lse = -inf.  q . K runs on the scaled FP4 x FP8 MFMA
+ * (the query split exactly into fp8 hi + lo parts, fp32 accumulation); the
+ * softmax weights are rounded to fp16 before the value product with V in fp16.
  *   q bf16 [B][Q][H][512]; cache as above; idx int32 [B][Q][top_k];
  *   count int32 [B][Q]; n_entries int32 [B]; q_pos int32 [B][Q] or NULL
  *   o fp32 [B][Q][H][512]; lse fp32 [B][Q][H] (natural log)
@@ -137,6 +138,21 @@ int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa
                    int Lw, float scale, const float* o_sparse, const float* lse_sparse,
                    float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_swa_merge_ws(int B, int Q, int H, int W);
+
+/* One attention layer in a single call: the sparse branch of csa2_sparse_attn
+ * and the window branch of csa2_swa_merge, merged by log-sum-exp (which is one
+ * softmax over the selected entries and the window tokens together).  Both
+ * branches write their split-K partials into ws and one combine pass produces
+ * out / lse_out; no intermediate sparse-only output exists.  Arguments as in
+ * the two calls above (q_pos also fixes the window, swa_pos0 NULL = 0).
+ *   out fp32 [B][Q][H][512]; lse_out fp32 [B][Q][H]
+ *   ws: >= csa2_attend_layer_ws(B, Q, H, top_k, W) bytes */
+int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
+                      const int32_t* count, const int32_t* n_entries, const int32_t* q_pos,
+                      const uint16_t* swa_kv, const int32_t* swa_len, const int32_t* swa_pos0,
+                      int B, int Q, int H, int cap, int top_k, int W, int Lw, float scale,
+                      float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream);
+size_t csa2_attend_layer_ws(int B, int Q, int H, int top_k, int W);
 
 /* Human-readable name of a status code (static string, host). */
 const char* csa2_status_str(int status);

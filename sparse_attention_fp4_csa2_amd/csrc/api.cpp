@@ -166,7 +166,7 @@ int csa2_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx
   AttnParams p{};
   p.q = q; p.cache = cache; p.idx = idx; p.count = count; p.n_entries = n_entries;
   p.top_k = top_k; p.cap = cap; p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows;
-  p.splits = splits;
+  p.splits = splits; p.out_splits = splits; p.split_base = 0;
   p.scale_log2 = scale * 1.4426950408889634f;
   hipStream_t st = as_stream(stream);
   if (splits == 1) {
@@ -185,7 +185,7 @@ int csa2_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx
 size_t csa2_swa_merge_ws(int B, int Q, int H, int W) {
   if (B <= 0 || Q <= 0 || H <= 0 || W <= 0) return 0;
   const int rows = B * Q;
-  const int s = attn_splits(rows, H, (W + 31) / 32);
+  const int s = window_splits(rows, H, (W + 31) / 32);
   return align_up((size_t)rows * s * H * CSA2_D * sizeof(float)) +
          align_up((size_t)rows * s * H * sizeof(float));
 }
@@ -205,10 +205,11 @@ int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa
   if (!ws || ws_bytes < need) return CSA2_ERR_WS_TOO_SMALL;
   if (!aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
   const int rows = B * Q;
-  const int splits = attn_splits(rows, H, (W + 31) / 32);
+  const int splits = window_splits(rows, H, (W + 31) / 32);
   AttnParams p{};
   p.q = q; p.swa = swa_kv; p.swa_len = swa_len; p.swa_pos0 = swa_pos0; p.W = W; p.Lw = Lw;
   p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows; p.splits = splits;
+  p.out_splits = splits; p.split_base = 0;
   p.scale_log2 = scale * 1.4426950408889634f;
   float* o_part = static_cast<float*>(ws);
   float* lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
@@ -217,6 +218,58 @@ int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa
   hipStream_t st = as_stream(stream);
   int rc = launch_attention(p, false, st);
   if (!rc) rc = launch_combine(o_part, lse_part, rows, splits, H, o_sparse, lse_sparse, out, lse_out, st);
+  return launch_status(rc);
+}
+
+size_t csa2_attend_layer_ws(int B, int Q, int H, int top_k, int W) {
+  if (B <= 0 || Q <= 0 || H <= 0 || top_k <= 0 || W <= 0) return 0;
+  const int rows = B * Q;
+  const int total = sparse_fp4_splits(rows, H, attn_n_tiles(top_k)) + window_splits(rows, H, (W + 31) / 32);
+  return align_up((size_t)rows * total * H * CSA2_D * sizeof(float)) +
+         align_up((size_t)rows * total * H * sizeof(float));
+}
+
+int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
+                      const int32_t* count, const int32_t* n_entries, const int32_t* q_pos,
+                      const uint16_t* swa_kv, const int32_t* swa_len, const int32_t* swa_pos0,
+                      int B, int Q, int H, int cap, int top_k, int W, int Lw, float scale,
+                      float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !cache || !idx || !count || !n_entries || !swa_kv || !swa_len || !out || !lse_out)
+    return CSA2_ERR_INVALID_ARG;
+  if (B <= 0 || Q <= 0 || H <= 0 || cap <= 0 || top_k <= 0 || W <= 0 || Lw <= 0)
+    return CSA2_ERR_INVALID_ARG;
+  if (cap % CSA2_BLOCK != 0 || !(scale > 0.f) || !isfinite(scale)) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(swa_kv, 16) || !aligned(out, 16))
+    return CSA2_ERR_INVALID_ARG;
+  if (H > CSA2_MAX_HEADS) return CSA2_ERR_UNSUPPORTED;
+  if ((size_t)cap / CSA2_BLOCK * CSA2_RECORD_BYTES > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
+  const size_t need = csa2_attend_layer_ws(B, Q, H, top_k, W);
+  if (!ws || ws_bytes < need) return CSA2_ERR_WS_TOO_SMALL;
+  if (!aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
+  const int rows = B * Q;
+  const int s_sparse = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
+  const int s_window = window_splits(rows, H, (W + 31) / 32);
+  const int total = s_sparse + s_window;
+  if (total > 128) return CSA2_ERR_UNSUPPORTED;
+  float* o_part = static_cast<float*>(ws);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                             align_up((size_t)rows * total * H * CSA2_D * sizeof(float)));
+  hipStream_t st = as_stream(stream);
+  AttnParams p{};
+  p.q = q; p.cache = cache; p.idx = idx; p.count = count; p.n_entries = n_entries;
+  p.top_k = top_k; p.cap = cap; p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.o_out = o_part; p.lse_out = lse_part; p.out_splits = total;
+  p.splits = s_sparse; p.split_base = 0;
+  int rc = launch_sparse_fp4(p, st);
+  if (!rc) {
+    AttnParams pw = p;
+    pw.cache = nullptr; pw.idx = nullptr; pw.count = nullptr; pw.n_entries = nullptr;
+    pw.swa = swa_kv; pw.swa_len = swa_len; pw.swa_pos0 = swa_pos0; pw.W = W; pw.Lw = Lw;
+    pw.splits = s_window; pw.split_base = s_sparse;
+    rc = launch_attention(pw, false, st);
+  }
+  if (!rc) rc = launch_combine(o_part, lse_part, rows, total, H, nullptr, nullptr, out, lse_out, st);
   return launch_status(rc);
 }
 

@@ -444,10 +444,10 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
   if (head_ok) {
     if (dh == 0 && hh == 0) {
       const float lse = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
-      p.lse_out[((size_t)row * p.splits + split) * p.H + head] = lse;
+      p.lse_out[((size_t)row * p.out_splits + p.split_base + split) * p.H + head] = lse;
     }
     const float f = FP4 ? ldexpf(il, vbase - VBIAS) : il;
-    float* dst = p.o_out + (((size_t)row * p.splits + split) * p.H + head) * D + 256 * dh + 4 * hh;
+    float* dst = p.o_out + (((size_t)row * p.out_splits + p.split_base + split) * p.H + head) * D + 256 * dh + 4 * hh;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -472,6 +472,17 @@ int attn_splits(int rows, int H, int n_tiles) {
   return s;
 }
 
+int window_splits(int rows, int H, int n_tiles) {
+  const int hgroups = (H + 63) / 64;
+  const int wgs = rows * hgroups;
+  int s = (128 + wgs - 1) / wgs;
+  const int cap_by_tiles = n_tiles / 4 > 1 ? n_tiles / 4 : 1;
+  if (s > cap_by_tiles) s = cap_by_tiles;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  return s;
+}
+
 int launch_attention(const AttnParams& p, bool fp4_source, hipStream_t stream) {
   const int hgroups = (p.H + 63) / 64;
   dim3 grid(p.splits, p.rows, hgroups);
@@ -481,6 +492,11 @@ int launch_attention(const AttnParams& p, bool fp4_source, hipStream_t stream) {
 }
 
 // ---- combine -----------------------------------------------------------
+// Log-sum-exp merge of the split-K partials (and an optional extra branch) of
+// one (row, head): wave 0 turns the partials' lse into weights in LDS, then
+// every thread streams its float4 of the 512 dims over all splits.
+constexpr int MAX_COMBINE_SPLITS = 128;
+
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       int splits, int H,
@@ -488,37 +504,61 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
                                                       const float* __restrict__ lse_ext,
                                                       float* __restrict__ out,
                                                       float* __restrict__ lse_out) {
+  __shared__ float wts[MAX_COMBINE_SPLITS + 1];
+  __shared__ float L_sh;
   const int h = blockIdx.x, row = blockIdx.y, t = threadIdx.x;
   const size_t rh = (size_t)row * H + h;
-  float m = -__builtin_inff();
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, lse_part[((size_t)row * splits + s) * H + h]);
-  const float le = o_ext ? lse_ext[rh] : -__builtin_inff();
-  m = fmaxf(m, le);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float L = -__builtin_inff();
-  if (m != -__builtin_inff()) {
+  const float* lp = lse_part + (size_t)row * splits * H + h;     // split s at lp[s * H]
+  if (t < 64) {
+    const float le = (o_ext && t == 0) ? lse_ext[rh] : -__builtin_inff();
+    float m = le;
+    for (int s = t; s < splits; s += 64) m = fmaxf(m, lp[(size_t)s * H]);
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
     float sum = 0.f;
-    for (int s = 0; s < splits; ++s) sum += expf(lse_part[((size_t)row * splits + s) * H + h] - m);
-    if (o_ext) sum += expf(le - m);
-    L = m + logf(sum);
-    for (int s = 0; s < splits; ++s) {
-      const size_t ps = ((size_t)row * splits + s) * H + h;
-      const float wgt = expf(lse_part[ps] - L);
-      if (wgt == 0.f) continue;
-      const float4 v = reinterpret_cast<const float4*>(o_part + ps * D)[t];
-      acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+    if (m != -__builtin_inff()) {
+      for (int s = t; s < splits; s += 64) sum += expf(lp[(size_t)s * H] - m);
+      if (t == 0 && o_ext) sum += expf(le - m);
     }
-    if (o_ext) {
-      const float wgt = expf(le - L);
-      if (wgt != 0.f) {
-        const float4 v = reinterpret_cast<const float4*>(o_ext + rh * D)[t];
-        acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
-      }
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) sum += __shfl_xor(sum, k, 64);
+    const float L = m == -__builtin_inff() ? -__builtin_inff() : m + logf(sum);
+    for (int s = t; s < splits; s += 64)
+      wts[s] = L == -__builtin_inff() ? 0.f : expf(lp[(size_t)s * H] - L);
+    if (t == 0) {
+      wts[splits] = (o_ext && L != -__builtin_inff()) ? expf(le - L) : 0.f;
+      L_sh = L;
+    }
+  }
+  __syncthreads();
+  const float4* src = reinterpret_cast<const float4*>(o_part + ((size_t)row * splits * H + h) * D) + t;
+  const size_t stride4 = (size_t)H * D / 4;                      // one split, in float4
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = 0;
+  for (; s + 4 <= splits; s += 4) {
+    const float4 v0 = src[(s + 0) * stride4], v1 = src[(s + 1) * stride4];
+    const float4 v2 = src[(s + 2) * stride4], v3 = src[(s + 3) * stride4];
+    const float w0 = wts[s], w1 = wts[s + 1], w2 = wts[s + 2], w3 = wts[s + 3];
+    acc.x += w0 * v0.x + w1 * v1.x + w2 * v2.x + w3 * v3.x;
+    acc.y += w0 * v0.y + w1 * v1.y + w2 * v2.y + w3 * v3.y;
+    acc.z += w0 * v0.z + w1 * v1.z + w2 * v2.z + w3 * v3.z;
+    acc.w += w0 * v0.w + w1 * v1.w + w2 * v2.w + w3 * v3.w;
+  }
+  for (; s < splits; ++s) {
+    const float4 v = src[s * stride4];
+    const float wv = wts[s];
+    acc.x += wv * v.x; acc.y += wv * v.y; acc.z += wv * v.z; acc.w += wv * v.w;
+  }
+  if (o_ext) {
+    const float we = wts[splits];
+    if (we != 0.f) {
+      const float4 v = reinterpret_cast<const float4*>(o_ext + rh * D)[t];
+      acc.x += we * v.x; acc.y += we * v.y; acc.z += we * v.z; acc.w += we * v.w;
     }
   }
   __syncthreads();   // o_ext may alias out: every read above precedes the writes below
   reinterpret_cast<float4*>(out + rh * D)[t] = acc;
-  if (t == 0) lse_out[rh] = L;
+  if (t == 0) lse_out[rh] = L_sh;
 }
 
 int launch_combine(const float* o_part, const float* lse_part, int rows, int splits, int H,

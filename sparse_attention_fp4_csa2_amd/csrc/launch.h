@@ -45,11 +45,15 @@ struct AttnParams {
   const int32_t* q_pos;     // [rows] or null
   int Q, H, rows, splits;
   float scale_log2;         // scale * log2(e)
-  float* o_out;             // [rows][splits][H][512] (final o when splits == 1)
-  float* lse_out;           // [rows][splits][H]
+  float* o_out;             // [rows][out_splits][H][512] (final o when out_splits == 1)
+  float* lse_out;           // [rows][out_splits][H]
+  int out_splits;           // split stride of o_out / lse_out (>= split_base + splits)
+  int split_base;           // this launch writes splits [split_base, split_base + splits)
 };
 
 int attn_splits(int rows, int H, int n_tiles);
+// bf16 window source: few tiles per row, so fewer, longer splits
+int window_splits(int rows, int H, int n_tiles);
 // MXFP4 source: 32-head workgroups, two per CU (sparse_fp4.hip)
 int sparse_fp4_splits(int rows, int H, int n_tiles);
 int launch_sparse_fp4(const AttnParams& p, hipStream_t stream);

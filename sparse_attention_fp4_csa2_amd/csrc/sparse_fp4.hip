@@ -433,10 +433,10 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     const float il = l > 0.f ? 1.f / l : 0.f;
     if (dq == 0 && hh == 0) {
       const float lse = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
-      p.lse_out[((size_t)row * p.splits + split) * p.H + head] = lse;
+      p.lse_out[((size_t)row * p.out_splits + p.split_base + split) * p.H + head] = lse;
     }
     const float f = ldexpf(il, base_o - VBIAS);
-    float* dst = p.o_out + (((size_t)row * p.splits + split) * p.H + head) * D + 128 * dq + 4 * hh;
+    float* dst = p.o_out + (((size_t)row * p.out_splits + p.split_base + split) * p.H + head) * D + 128 * dq + 4 * hh;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll

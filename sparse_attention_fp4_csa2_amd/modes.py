@@ -64,6 +64,7 @@ class LayerBuffers:
         self.ws_index = _ws(_lib.index_topk_ws(B, Q, cap, top_groups), dev)
         self.ws_attn = _ws(_lib.sparse_attn_ws(B, Q, H, top_k), dev)
         self.ws_swa = _ws(_lib.swa_merge_ws(B, Q, H, W), dev)
+        self.ws_layer = _ws(_lib.attend_layer_ws(B, Q, H, top_k, W), dev)
 
 
 def _ws(nbytes, dev):
@@ -77,9 +78,20 @@ def index(buf, cache, q_idx, w, q_pos=None, stream=None):
 
 
 def attend(buf, cache, q, swa, swa_len, idx=None, count=None, swa_pos0=None, q_pos=None,
-           scale=SCALE, stream=None):
+           scale=SCALE, stream=None, fused=True):
+    """Sparse + window branches merged into buf.out / buf.lse_out.
+
+    fused=True: one csa2_attend_layer call (one combine over both branches'
+    split-K partials).  fused=False: csa2_sparse_attn (buf.o, buf.lse) then
+    csa2_swa_merge.
+    """
     idx = buf.idx if idx is None else idx
     count = buf.count if count is None else count
+    if fused:
+        _lib.attend_layer(q, cache.records, idx, count, cache.n_entries, swa, swa_len, buf.W, scale,
+                          buf.out, buf.lse_out, buf.ws_layer, swa_pos0=swa_pos0, q_pos=q_pos,
+                          stream=stream)
+        return
     _lib.sparse_attn(q, cache.records, idx, count, cache.n_entries, scale, buf.o, buf.lse,
                      ws=buf.ws_attn, q_pos=q_pos, stream=stream)
     _lib.swa_merge(q, swa, swa_len, buf.W, scale, buf.o, buf.lse, buf.out, buf.lse_out,

@@ -263,3 +263,68 @@ def test_repeat_runs_bitwise_identical():
     outs = [gpu_sparse(x.q, cache, idx, np.array([[cfg.K]]), x.n_entries) for _ in range(5)]
     for o, l in outs[1:]:
         assert o.tobytes() == outs[0][0].tobytes() and l.tobytes() == outs[0][1].tobytes()
+
+
+def gpu_layer(q, cache, idx, count, n_entries, swa, swa_len, W, swa_pos0=None, q_pos=None):
+    lib = _lib()
+    B, Q, H = q.shape[:3]
+    out = torch.full((B, Q, H, 512), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, Q, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lib.attend_layer_ws(B, Q, H, idx.shape[-1], W), dtype=torch.uint8, device="cuda")
+    lib.attend_layer(dev_bf16(q), cache, dev(np.ascontiguousarray(idx, np.int32)),
+                     dev(np.asarray(count, np.int32)), dev(np.asarray(n_entries, np.int32)), dev_bf16(swa),
+                     dev(np.asarray(swa_len, np.int32)), W, SCALE, out, lse, ws,
+                     swa_pos0=None if swa_pos0 is None else dev(np.asarray(swa_pos0, np.int32)),
+                     q_pos=None if q_pos is None else dev(np.asarray(q_pos, np.int32)))
+    torch.cuda.synchronize()
+    return host(out), host(lse)
+
+
+@pytest.mark.parametrize("H", [16, 40, 64, 128])
+def test_attend_layer_decode_matches_joint_softmax(H):
+    # one call: sparse branch + window branch, checked against the oracle's
+    # sparse attention, window attention and merge (= one softmax over both sets)
+    rng = rng_for(30 + H)
+    B, N, K, W, Lw = 3, 2048, 64, 128, 160
+    latent = normal_bf16(rng, (B, N, 512))
+    cache = gpu_cache(latent, N)
+    cache_np = [mxfp4.build_records(latent[b], N) for b in range(B)]
+    q = normal_bf16(rng, (B, 1, H, 512))
+    swa = normal_bf16(rng, (B, Lw, 512))
+    swa_len = np.array([160, 128, 9], np.int32)
+    n_entries = np.array([2048, 1999, 2048], np.int32)
+    idx = np.full((B, 1, K), -1, np.int32)
+    count = np.array([[K], [37], [0]], np.int32)             # full, ragged, empty selection
+    for b in range(B):
+        c = int(count[b, 0])
+        if c:
+            idx[b, 0, :c] = np.sort(rng.choice(N // 8, c, replace=False))
+    out, lse = gpu_layer(q, cache, idx, count, n_entries, swa, swa_len, W)
+    ro = np.zeros((B, 1, H, 512))
+    rl = np.zeros((B, 1, H))
+    for b in range(B):
+        ro[b, 0], rl[b, 0] = modes.attend_row(q[b, 0], cache_np[b], idx[b, 0], int(count[b, 0]),
+                                              int(n_entries[b]), swa[b], int(swa_len[b]), W)
+    assert_close_rms(out, ro)
+    assert_lse_close(lse, rl)
+
+
+def test_attend_layer_causal_rows():
+    rng = rng_for(41)
+    B, Q, H, N, K, W = 1, 6, 64, 4096, 96, 32
+    latent = normal_bf16(rng, (B, N, 512))
+    cache = gpu_cache(latent, N)
+    cache_np = mxfp4.build_records(latent[0], N)
+    q = normal_bf16(rng, (B, Q, H, 512))
+    pos0 = 2 * N - 40
+    Lw = 80
+    swa = normal_bf16(rng, (B, Lw, 512))
+    q_pos = np.array([[2 * N - 40, 2 * N - 20, 2 * N - 1, 2 * N + 30, 3000, 2 * N + 39]], np.int32)
+    idx = np.stack([np.sort(rng.choice(N // 8, K, replace=False)) for _ in range(Q)])[None].astype(np.int32)
+    count = np.full((B, Q), K, np.int32)
+    out, lse = gpu_layer(q, cache, idx, count, [N], swa, [Lw], W, swa_pos0=[pos0], q_pos=q_pos)
+    for r in range(Q):
+        ro, rl = modes.attend_row(q[0, r], cache_np, idx[0, r], K, N, swa[0], Lw, W,
+                                  q_pos=int(q_pos[0, r]), swa_pos0=pos0)
+        assert_close_rms(out[0, r], ro, what=f"row {r}")
+        assert_lse_close(lse[0, r], rl)
