@@ -220,43 +220,46 @@ __global__ __launch_bounds__(256) void index_rows_kernel(
   if (e < e_end) score(e, k0);
 }
 
-// Coarse scores: one workgroup per row, one thread per group at a time.
+// Coarse scores: grid (groups / 32, rows); thread (group t/8, head t%8) forms
+// the dot product of the head's query with the group's mean key (fp32 sum /
+// count) and the 8 heads of a group meet by lane shuffles.
+constexpr int GROUPS_PER_WG = 32;
+
 __global__ __launch_bounds__(256) void group_scores_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const float* __restrict__ group_sum, const int32_t* __restrict__ n_entries, int Q, int Hi,
     int cap, float* __restrict__ gscores) {
-  __shared__ float qs[MAX_HI][DI];
-  __shared__ float ws[MAX_HI];
-  const int row = blockIdx.x, b = row / Q;
-  for (int i = threadIdx.x; i < Hi * DI; i += 256)
-    qs[i / DI][i % DI] = bf16_to_f32(q_idx[(size_t)row * Hi * DI + i]);
-  if (threadIdx.x < Hi) ws[threadIdx.x] = w[(size_t)row * Hi + threadIdx.x];
-  __syncthreads();
+  const int row = blockIdx.y, b = row / Q;
   const int G = cap / GROUP_ENTRIES;
   const int ne = min(n_entries[b], cap);
-  for (int g = threadIdx.x; g < G; g += 256) {
-    const int cnt = min(GROUP_ENTRIES, ne - g * GROUP_ENTRIES);
-    float s = -__builtin_inff();
-    if (cnt > 0) {
-      const float inv = 1.f / (float)cnt;
-      const float4* gs = reinterpret_cast<const float4*>(group_sum + ((size_t)b * G + g) * DI);
-      float mean[DI];
+  const int t = threadIdx.x;
+  const int g = blockIdx.x * GROUPS_PER_WG + (t >> 3);
+  const int h0 = t & 7;
+  float s = 0.f;
+  const int cnt = g < G ? min(GROUP_ENTRIES, ne - g * GROUP_ENTRIES) : 0;
+  if (cnt > 0) {
+    const float4* gs = reinterpret_cast<const float4*>(group_sum + ((size_t)b * G + g) * DI);
+    float4 m4[DI / 4];
+#pragma unroll
+    for (int d4 = 0; d4 < DI / 4; ++d4) m4[d4] = gs[d4];
+    const float inv = 1.f / (float)cnt;
+    // heads h0, h0 + 8 (Hi <= 16)
+    for (int h = h0; h < Hi; h += 8) {
+      const uint16_t* qh = q_idx + ((size_t)row * Hi + h) * DI;
+      float dot = 0.f;
 #pragma unroll
       for (int d4 = 0; d4 < DI / 4; ++d4) {
-        const float4 v = gs[d4];
-        mean[4 * d4] = v.x * inv; mean[4 * d4 + 1] = v.y * inv;
-        mean[4 * d4 + 2] = v.z * inv; mean[4 * d4 + 3] = v.w * inv;
+        const uint2 qq = *reinterpret_cast<const uint2*>(qh + 4 * d4);
+        dot += __uint_as_float(qq.x << 16) * m4[d4].x + __uint_as_float(qq.x & 0xFFFF0000u) * m4[d4].y +
+               __uint_as_float(qq.y << 16) * m4[d4].z + __uint_as_float(qq.y & 0xFFFF0000u) * m4[d4].w;
       }
-      s = 0.f;
-      for (int h = 0; h < Hi; ++h) {
-        float dot = 0.f;
-#pragma unroll
-        for (int d = 0; d < DI; ++d) dot += qs[h][d] * mean[d];
-        s += ws[h] * fmaxf(dot, 0.f);
-      }
+      s += w[(size_t)row * Hi + h] * fmaxf(dot * inv, 0.f);
     }
-    gscores[(size_t)row * G + g] = s;
   }
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 4, 64);
+  if (h0 == 0 && g < G) gscores[(size_t)row * G + g] = cnt > 0 ? s : -__builtin_inff();
 }
 
 int launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* key_cache,
@@ -285,8 +288,9 @@ int launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k
 int launch_group_scores(const uint16_t* q_idx, const float* w, const float* group_sum,
                         const int32_t* n_entries, int B, int Q, int Hi, int cap, float* gscores,
                         hipStream_t stream) {
-  group_scores_kernel<<<B * Q, 256, 0, stream>>>(q_idx, w, group_sum, n_entries, Q, Hi, cap,
-                                                 gscores);
+  const int G = cap / GROUP_ENTRIES;
+  dim3 grid((G + GROUPS_PER_WG - 1) / GROUPS_PER_WG, B * Q);
+  group_scores_kernel<<<grid, 256, 0, stream>>>(q_idx, w, group_sum, n_entries, Q, Hi, cap, gscores);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
