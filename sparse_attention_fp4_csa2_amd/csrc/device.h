@@ -36,6 +36,7 @@ __device__ __forceinline__ float warp_max_xor(float v, int lo_mask_bits) {
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s);
   if (s != s || s == -__builtin_inff()) return 0u;
+  if (s == 0.0f) return 0x80000000u;          // -0 and +0 are one score (a tie)
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -6,10 +6,15 @@
 // scores) ordered by score descending, then block id ascending; keep the first
 // min(K, #candidates); emit them ascending by block id, -1 padded, with a count.
 //
-// One 1024-thread workgroup per row: an exact radix select (11 + 11 + 10 bits)
-// over order-preserving 32-bit keys finds the K-th largest key tau, then a
-// block-wide scan compacts the ids with key > tau, plus the lowest-id ties at
-// tau, in id order.  The keys are read once and stay in registers.
+// One workgroup per row, keys read once into registers (C per thread, fixed at
+// compile time).  Exact radix select on order-preserving 32-bit keys, taken
+// relative to the row's smallest candidate key lo: the digits of key - lo + 1
+// start at the top bit of max - lo + 1, so the first 2048-bin histogram spreads
+// over the range the row's scores actually occupy (a fixed top-11-bit digit
+// puts a typical row into a handful of bins, and the LDS atomics on those few
+// bins serialise).  Each pass fixes up to 11 more bits of the K-th largest
+// key; then a block-wide scan compacts the ids with key > tau, plus the
+// lowest-id ties at tau, in id order.
 #include "device.h"
 #include "launch.h"
 
@@ -17,117 +22,177 @@ namespace csa2 {
 
 namespace {
 
-constexpr int TPB = 1024;
+constexpr int HIST_BINS = 2048;
 
-// Exclusive scan of one value per thread across the 1024-thread block.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sbuf, uint32_t* total) {
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  // inclusive scan inside the wave
-  uint32_t x = v;
+// Wave-wide inclusive prefix sum: four DPP row shifts (1, 2, 4, 8) within each
+// 16-lane row, then row broadcasts of lane 15 and lane 31.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
+// Exclusive scan of one value per thread across the block; *total = block sum.
+template <int TPB>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sbuf, uint32_t* total) {
+  constexpr int NW = TPB / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) sbuf[wv] = inc;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sbuf[wv] = x;
-  __syncthreads();
-  if (t < 64) {
-    uint32_t s = t < TPB / 64 ? sbuf[t] : 0u;
-    uint32_t inc = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = (uint32_t)__shfl_up((int)inc, o, 64);
-      if (t >= o) inc += y;
-    }
-    if (t < TPB / 64) sbuf[32 + t] = inc - s;     // exclusive wave offsets
-    if (t == TPB / 64 - 1) sbuf[63] = inc;         // block total
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t x = sbuf[w];
+    off += w < wv ? x : 0u;
+    tot += x;
   }
   __syncthreads();
-  const uint32_t res = x - v + sbuf[32 + wv];
-  *total = sbuf[63];
-  __syncthreads();
-  return res;
+  *total = tot;
+  return off + inc - v;
 }
 
 }  // namespace
 
-// Thread t holds the keys of positions [t*C, t*C + C) in registers (C fixed at
-// compile time), so the scores are read from memory once.
-template <int C>
-__global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ scores, int n, int k,
+// RANGE: digits relative to the row's key range (min/max reduction first);
+// otherwise fixed digits from bit 31 (11 + 11 + 10 bits), which skips the
+// reduction and pays off when the scores spread over many bins anyway.
+template <int TPB, int C, bool RANGE>
+__global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ scores, int n, int k, int vec,
                                                    const int32_t* __restrict__ gsel, int n_gsel,
                                                    int32_t* __restrict__ idx,
                                                    int32_t* __restrict__ count) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t sbuf[64];
+  constexpr int NW = TPB / 64;
+  constexpr int BPT = HIST_BINS / TPB;      // histogram bins scanned per thread
+  __shared__ uint32_t hist[HIST_BINS];
+  __shared__ uint32_t sbuf[NW];
+  __shared__ uint32_t sred[NW][3];
   __shared__ uint32_t sh_digit, sh_above;
-  const int row = blockIdx.x, t = threadIdx.x;
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const float* s = scores + (size_t)row * n;
   const int i0 = t * C;
 
   uint32_t key[C];
 #pragma unroll
-  for (int c = 0; c < C; ++c) key[c] = i0 + c < n ? score_key(s[i0 + c]) : 0u;
+  for (int c = 0; c < C; c += 4) {
+    if (vec && i0 + c + 3 < n) {
+      const float4 v = *reinterpret_cast<const float4*>(s + i0 + c);
+      key[c] = score_key(v.x), key[c + 1] = score_key(v.y);
+      key[c + 2] = score_key(v.z), key[c + 3] = score_key(v.w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[c + j] = i0 + c + j < n ? score_key(s[i0 + c + j]) : 0u;
+    }
+  }
 
+  bool all = false;               // every candidate is kept (block-uniform)
   uint32_t prefix = 0, kleft = (uint32_t)k;
-  bool all = false;          // every candidate is selected
-  const int shifts[3] = {21, 10, 0};
-  const int nbits[3] = {11, 11, 10};
+  int pos = 32;
+  if constexpr (RANGE) {
+    // candidate count and key range of the row
+    uint32_t kmin = 0xffffffffu, kmax = 0u, nv = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      if (key[c]) {
+        kmin = min(kmin, key[c]);
+        kmax = max(kmax, key[c]);
+        ++nv;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+      nv += (uint32_t)__shfl_xor((int)nv, o, 64);
+    }
+    if (lane == 0) sred[wv][0] = kmin, sred[wv][1] = kmax, sred[wv][2] = nv;
+    __syncthreads();
+    kmin = 0xffffffffu, kmax = 0u, nv = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      kmin = min(kmin, sred[w][0]);
+      kmax = max(kmax, sred[w][1]);
+      nv += sred[w][2];
+    }
+    all = nv <= (uint32_t)k;
+    // from here on key[c] holds x = key - kmin + 1 for a candidate (no wrap:
+    // kmin >= 1), 0 for a non-candidate
+#pragma unroll
+    for (int c = 0; c < C; ++c) key[c] = key[c] ? key[c] - kmin + 1u : 0u;
+    pos = all ? 0 : 32 - __clz(kmax - kmin + 1u);
+  }
+
+  // radix select on x (x = key without RANGE), from bit pos - 1 down
 #pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = shifts[pass], nb = 1 << nbits[pass];
-    const int hi_shift = sh + nbits[pass];          // bits above this digit are decided
+  while (pos > 0) {
+    const int sh = pos > 11 ? pos - 11 : 0;
+    const int nb = 1 << (pos - sh);
+    const uint32_t hmask = pos >= 32 ? 0u : (~0u << pos);   // bits already decided
     for (int i = t; i < nb; i += TPB) hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const bool match = hi_shift >= 32 ? true : ((key[c] >> hi_shift) == (prefix >> hi_shift));
-      if (key[c] != 0u && match) atomicAdd(&hist[(key[c] >> sh) & (nb - 1)], 1u);
+      const uint32_t x = key[c];
+      if (x && (x & hmask) == prefix) atomicAdd(&hist[(x >> sh) & (nb - 1)], 1u);
     }
     __syncthreads();
-    // suffix counts from the top bin: thread t owns reversed bins 2t, 2t+1
-    const int r0 = 2 * t, r1 = 2 * t + 1;
-    const uint32_t h0 = r0 < nb ? hist[nb - 1 - r0] : 0u;
-    const uint32_t h1 = r1 < nb ? hist[nb - 1 - r1] : 0u;
+    // thread t owns the reversed bins BPT*t .. BPT*t + BPT - 1 (counted from the top)
+    uint32_t h[BPT], hs = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int r = BPT * t + j;
+      h[j] = r < nb ? hist[nb - 1 - r] : 0u;
+      hs += h[j];
+    }
     uint32_t tot;
-    const uint32_t before = block_exclusive_scan(h0 + h1, sbuf, &tot);
-    if (pass == 0 && tot <= kleft) { all = true; break; }      // uniform: tot is block-wide
-    if (r0 < nb && before < kleft && kleft <= before + h0) { sh_digit = nb - 1 - r0; sh_above = before; }
-    if (r1 < nb && before + h0 < kleft && kleft <= before + h0 + h1) {
-      sh_digit = nb - 1 - r1; sh_above = before + h0;
+    uint32_t before = block_excl_scan<TPB>(hs, sbuf, &tot);
+    if (!RANGE && pos == 32 && tot <= kleft) {      // at most k candidates
+      all = true;
+      break;
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int r = BPT * t + j;
+      if (r < nb && before < kleft && kleft <= before + h[j]) sh_digit = nb - 1 - r, sh_above = before;
+      before += h[j];
     }
     __syncthreads();
     prefix |= sh_digit << sh;
     kleft -= sh_above;
-    __syncthreads();
+    pos = sh;
   }
-  const uint32_t tau = all ? 0u : prefix;            // select key > tau, plus need_eq ties at tau
+  // keep x > tau, plus the first need_eq candidates (in id order) with x == tau;
+  // tau >= 1 unless every candidate is kept, when tau = 0 keeps all x >= 1
+  const uint32_t tau = all ? 0u : prefix;
   const uint32_t need_eq = all ? 0u : kleft;
 
-  // compaction in id order
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     gt += key[c] > tau;
-    eq += (key[c] == tau && tau != 0u);
+    eq += key[c] == tau;
   }
   uint32_t tot_gt, tot_eq;
-  const uint32_t gt_pre = block_exclusive_scan(gt, sbuf, &tot_gt);
-  const uint32_t eq_pre = block_exclusive_scan(eq, sbuf, &tot_eq);
-  uint32_t pos = gt_pre + min(eq_pre, need_eq);
+  const uint32_t gt_pre = block_excl_scan<TPB>(gt, sbuf, &tot_gt);
+  const uint32_t eq_pre = block_excl_scan<TPB>(eq, sbuf, &tot_eq);
+  uint32_t pos_out = gt_pre + min(eq_pre, need_eq);
   uint32_t eq_seen = eq_pre;
   int32_t* out = idx + (size_t)row * k;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     bool sel = key[c] > tau;
-    if (!sel && key[c] == tau && tau != 0u) {
+    if (key[c] == tau) {
       sel = eq_seen < need_eq;
       ++eq_seen;
     }
     if (sel) {
       const int i = i0 + c;
       const int id = gsel ? gsel[(size_t)row * n_gsel + i / 64] * 64 + (i & 63) : i;
-      out[pos++] = id;
+      out[pos_out++] = id;
     }
   }
   const uint32_t total = tot_gt + min(tot_eq, need_eq);
@@ -135,14 +200,22 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ sco
   if (t == 0) count[row] = (int32_t)total;
 }
 
+// n <= 65536.  Rows of up to 8192 scores run on 256 threads with fixed
+// digits; longer rows use 1024 threads and range-relative digits when there
+// are too few rows to fill the chip (there one row's latency is the cost, and
+// candidates drawn from a few top groups crowd into few fixed-digit bins).
 int launch_topk(const float* scores, int rows, int n, int k, const int32_t* gsel, int n_gsel,
                 int32_t* idx, int32_t* count, hipStream_t stream) {
-  const int per = (n + TPB - 1) / TPB;
-  if (per <= 1) topk_kernel<1><<<rows, TPB, 0, stream>>>(scores, n, k, gsel, n_gsel, idx, count);
-  else if (per <= 4) topk_kernel<4><<<rows, TPB, 0, stream>>>(scores, n, k, gsel, n_gsel, idx, count);
-  else if (per <= 8) topk_kernel<8><<<rows, TPB, 0, stream>>>(scores, n, k, gsel, n_gsel, idx, count);
-  else if (per <= 16) topk_kernel<16><<<rows, TPB, 0, stream>>>(scores, n, k, gsel, n_gsel, idx, count);
-  else topk_kernel<64><<<rows, TPB, 0, stream>>>(scores, n, k, gsel, n_gsel, idx, count);
+  const int vec = (n % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
+#define CSA2_TOPK(T, C, R) \
+  topk_kernel<T, C, R><<<rows, T, 0, stream>>>(scores, n, k, vec, gsel, n_gsel, idx, count)
+  if (n <= 256 * 4) CSA2_TOPK(256, 4, false);
+  else if (n <= 256 * 16) CSA2_TOPK(256, 16, false);
+  else if (n <= 256 * 32) CSA2_TOPK(256, 32, false);
+  else if (n <= 256 * 64 && rows >= 128) CSA2_TOPK(256, 64, false);
+  else if (n <= 1024 * 16) CSA2_TOPK(1024, 16, true);
+  else CSA2_TOPK(1024, 64, true);
+#undef CSA2_TOPK
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -32,7 +32,7 @@ def gpu_topk(scores, k):
                                  (1000, 1), (65536, 2048)])
 def test_topk_from_scores_bit_exact_with_ties(n, k):
     rng = rng_for(n * 7 + k)
-    rows = 6
+    rows = 7
     s = np.empty((rows, n), dtype=np.float32)
     s[0] = rng.standard_normal(n)
     s[1] = rng.integers(-3, 4, size=n)                 # heavy ties, negatives, zeros
@@ -43,6 +43,8 @@ def test_topk_from_scores_bit_exact_with_ties(n, k):
     s[4, :min(n, 5)] = [0.0, -0.0, 2.0, -1.0, 2.0][:min(n, 5)]   # fewer candidates than k
     s[5] = np.float32(1e30) * rng.standard_normal(n).astype(np.float32)
     s[5, ::5] = np.nan                                  # NaN = non-candidate
+    s[6] = rng.choice(np.array([0.0, -0.0], np.float32), n)   # +0 and -0 tie; rank k among them
+    s[6, rng.choice(n, max(1, min(n, k) // 2), replace=False)] = 1.0
     got, cnt = gpu_topk(s, k)
     for r in range(rows):
         ref_in = np.where(np.isnan(s[r]), -np.inf, s[r]).astype(np.float64)
