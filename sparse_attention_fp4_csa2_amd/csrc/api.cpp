@@ -216,7 +216,7 @@ int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa
                                              align_up((size_t)rows * splits * H * CSA2_D * sizeof(float)));
   p.o_out = o_part; p.lse_out = lse_part;
   hipStream_t st = as_stream(stream);
-  int rc = launch_attention(p, false, st);
+  int rc = launch_window(p, st);
   if (!rc) rc = launch_combine(o_part, lse_part, rows, splits, H, o_sparse, lse_sparse, out, lse_out, st);
   return launch_status(rc);
 }
@@ -267,7 +267,7 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
     pw.cache = nullptr; pw.idx = nullptr; pw.count = nullptr; pw.n_entries = nullptr;
     pw.swa = swa_kv; pw.swa_len = swa_len; pw.swa_pos0 = swa_pos0; pw.W = W; pw.Lw = Lw;
     pw.splits = s_window; pw.split_base = s_sparse;
-    rc = launch_attention(pw, false, st);
+    rc = launch_window(pw, st);
   }
   if (!rc) rc = launch_combine(o_part, lse_part, rows, total, H, nullptr, nullptr, out, lse_out, st);
   return launch_status(rc);

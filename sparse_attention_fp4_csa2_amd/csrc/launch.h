@@ -51,13 +51,12 @@ struct AttnParams {
   int split_base;           // this launch writes splits [split_base, split_base + splits)
 };
 
-int attn_splits(int rows, int H, int n_tiles);
-// bf16 window source: few tiles per row, so fewer, longer splits
+// bf16 window (attention.hip): 64-head workgroups, few tiles per row
 int window_splits(int rows, int H, int n_tiles);
-// MXFP4 source: 32-head workgroups, two per CU (sparse_fp4.hip)
+int launch_window(const AttnParams& p, hipStream_t stream);
+// MXFP4 selected blocks (sparse_fp4.hip): 32-head workgroups, two per CU
 int sparse_fp4_splits(int rows, int H, int n_tiles);
 int launch_sparse_fp4(const AttnParams& p, hipStream_t stream);
-int launch_attention(const AttnParams& p, bool fp4_source, hipStream_t stream);
 
 // Merge split partials (and an optional extra branch) -> out [rows][H][512], lse [rows][H].
 int launch_combine(const float* o_part, const float* lse_part, int rows, int splits, int H,
