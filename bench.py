@@ -6,6 +6,9 @@ One step = the whole hot path over one batch of synthetic input:
             sliding window, merged by one log-sum-exp combine)
   prefill   csa2_append_fp4 (the chunk's 2048 entries) -> csa2_index_topk (causal,
             every query row) -> csa2_attend_layer (causal window)
+All calls run on one stream: running the window branch on a second stream
+beside the indexer (csa2_attend_layer_window / _sparse) measured no faster,
+as the two contend for HBM and CUs.
 Default workload (--config decode64k): decode at 64K context, 32 sequences, 64
 heads, 32768 MXFP4 entries = 4096 blocks of 8 per sequence, 8 x 64 indexer,
 top-K 2048, window 512; seeded N(0,1) bf16 inputs with planted relevant blocks.
@@ -316,7 +319,8 @@ def main():
         "fp4_kv_read_TBps": round(kv_tbps, 3),
         "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
         "launches_per_step": per_step,
-        "compute": "MXFP4 cache dequantised to fp16 for fp16 MFMA, fp32 accumulate; window in bf16",
+        "compute": ("Q.K on the scaled FP4 x FP8 MFMA (query split into fp8 hi + lo), P.V on fp16 MFMA "
+                    "with the MXFP4 values dequantised to fp16, fp32 accumulate; window in bf16"),
         "roofline": {"kernel": "csa2_sparse_attn (attention + split-K combine)", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_FP16_TFLOPS, 4),

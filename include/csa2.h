@@ -154,6 +154,28 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
                       float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_attend_layer_ws(int B, int Q, int H, int top_k, int W);
 
+/* csa2_attend_layer in two phases, so that the window branch -- which needs no
+ * selection -- can run on a second stream while the indexer and top-K run.
+ * The results are identical to csa2_attend_layer's (same kernels, same split
+ * slots in ws).
+ * Phase 1, csa2_attend_layer_window: the window branch's split-K partials into
+ * ws (a workspace of csa2_attend_layer_ws(B, Q, H, top_k, W) bytes).
+ * Phase 2, csa2_attend_layer_sparse: the sparse branch's partials into the same
+ * ws, then the combine of both into out / lse_out.  Phase 1 on the same ws must
+ * be complete before phase 2 starts on its stream: the caller orders them
+ * (same stream, or an event recorded after phase 1 and waited on by phase 2's
+ * stream).  Phase 2 must also complete before phase 1 of a later call reuses
+ * ws.  Arguments as in csa2_attend_layer; top_k and W must match between the
+ * two phases (they fix the split layout of ws). */
+int csa2_attend_layer_window(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa_len,
+                             const int32_t* swa_pos0, const int32_t* q_pos, int B, int Q, int H,
+                             int top_k, int W, int Lw, float scale, void* ws, size_t ws_bytes,
+                             void* stream);
+int csa2_attend_layer_sparse(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
+                             const int32_t* count, const int32_t* n_entries, const int32_t* q_pos,
+                             int B, int Q, int H, int cap, int top_k, int W, float scale,
+                             float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static string, host). */
 const char* csa2_status_str(int status);
 /* Library version: major * 10000 + minor * 100 + patch. */

@@ -34,6 +34,9 @@ _SIGS = {
     "csa2_attend_layer": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                _P, _P, _P, _SZ, _P]),
     "csa2_attend_layer_ws": (_SZ, [_I, _I, _I, _I, _I]),
+    "csa2_attend_layer_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
+    "csa2_attend_layer_sparse": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P,
+                                      _SZ, _P]),
     "csa2_status_str": (ctypes.c_char_p, [_I]),
     "csa2_version": (_I, []),
 }
@@ -200,6 +203,38 @@ def attend_layer(q, cache, idx, count, n_entries, swa_kv, swa_len, W, scale, out
                                _ptr(lse_out, torch.float32, "lse_out"), _ptr(ws, None, "ws"),
                                ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "csa2_attend_layer")
+
+
+def attend_layer_window(q, swa_kv, swa_len, top_k, W, scale, ws, swa_pos0=None, q_pos=None,
+                        stream=None):
+    """csa2_attend_layer_window: the window branch's split-K partials into ws (phase 1)."""
+    lib = load()
+    B, Q, H = q.shape[0], q.shape[1], q.shape[2]
+    Lw = swa_kv.shape[1]
+    rc = lib.csa2_attend_layer_window(_bf16_ptr(q, "q"), _bf16_ptr(swa_kv, "swa_kv"),
+                                      _ptr(swa_len, torch.int32, "swa_len"),
+                                      _ptr(swa_pos0, torch.int32, "swa_pos0"),
+                                      _ptr(q_pos, torch.int32, "q_pos"), B, Q, H, top_k, W, Lw,
+                                      float(scale), _ptr(ws, None, "ws"), ws.numel() * ws.element_size(),
+                                      _stream(stream))
+    _check(rc, "csa2_attend_layer_window")
+
+
+def attend_layer_sparse(q, cache, idx, count, n_entries, W, scale, out, lse_out, ws, q_pos=None,
+                        stream=None):
+    """csa2_attend_layer_sparse: sparse partials into ws, then the combine of both (phase 2)."""
+    lib = load()
+    B, Q, H = q.shape[0], q.shape[1], q.shape[2]
+    cap = cache.shape[1] * BLOCK
+    top_k = idx.shape[-1]
+    rc = lib.csa2_attend_layer_sparse(_bf16_ptr(q, "q"), _ptr(cache, torch.uint8, "cache"),
+                                      _ptr(idx, torch.int32, "idx"), _ptr(count, torch.int32, "count"),
+                                      _ptr(n_entries, torch.int32, "n_entries"),
+                                      _ptr(q_pos, torch.int32, "q_pos"), B, Q, H, cap, top_k, W,
+                                      float(scale), _ptr(out, torch.float32, "out"),
+                                      _ptr(lse_out, torch.float32, "lse_out"), _ptr(ws, None, "ws"),
+                                      ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "csa2_attend_layer_sparse")
 
 
 def version():

@@ -229,18 +229,42 @@ size_t csa2_attend_layer_ws(int B, int Q, int H, int top_k, int W) {
          align_up((size_t)rows * total * H * sizeof(float));
 }
 
-int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
-                      const int32_t* count, const int32_t* n_entries, const int32_t* q_pos,
-                      const uint16_t* swa_kv, const int32_t* swa_len, const int32_t* swa_pos0,
-                      int B, int Q, int H, int cap, int top_k, int W, int Lw, float scale,
-                      float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
-  if (!q || !cache || !idx || !count || !n_entries || !swa_kv || !swa_len || !out || !lse_out)
-    return CSA2_ERR_INVALID_ARG;
-  if (B <= 0 || Q <= 0 || H <= 0 || cap <= 0 || top_k <= 0 || W <= 0 || Lw <= 0)
-    return CSA2_ERR_INVALID_ARG;
+int csa2_attend_layer_window(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa_len,
+                             const int32_t* swa_pos0, const int32_t* q_pos, int B, int Q, int H,
+                             int top_k, int W, int Lw, float scale, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!q || !swa_kv || !swa_len) return CSA2_ERR_INVALID_ARG;
+  if (B <= 0 || Q <= 0 || H <= 0 || top_k <= 0 || W <= 0 || Lw <= 0) return CSA2_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(swa_kv, 16)) return CSA2_ERR_INVALID_ARG;
+  if (H > CSA2_MAX_HEADS) return CSA2_ERR_UNSUPPORTED;
+  const size_t need = csa2_attend_layer_ws(B, Q, H, top_k, W);
+  if (!ws || ws_bytes < need) return CSA2_ERR_WS_TOO_SMALL;
+  if (!aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
+  const int rows = B * Q;
+  const int s_sparse = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
+  const int s_window = window_splits(rows, H, (W + 31) / 32);
+  const int total = s_sparse + s_window;
+  if (total > 128) return CSA2_ERR_UNSUPPORTED;
+  AttnParams pw{};
+  pw.q = q; pw.swa = swa_kv; pw.swa_len = swa_len; pw.swa_pos0 = swa_pos0; pw.W = W; pw.Lw = Lw;
+  pw.q_pos = q_pos; pw.Q = Q; pw.H = H; pw.rows = rows;
+  pw.scale_log2 = scale * 1.4426950408889634f;
+  pw.o_out = static_cast<float*>(ws);
+  pw.lse_out = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                        align_up((size_t)rows * total * H * CSA2_D * sizeof(float)));
+  pw.out_splits = total; pw.splits = s_window; pw.split_base = s_sparse;
+  return launch_status(launch_window(pw, as_stream(stream)));
+}
+
+int csa2_attend_layer_sparse(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
+                             const int32_t* count, const int32_t* n_entries, const int32_t* q_pos,
+                             int B, int Q, int H, int cap, int top_k, int W, float scale,
+                             float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !cache || !idx || !count || !n_entries || !out || !lse_out) return CSA2_ERR_INVALID_ARG;
+  if (B <= 0 || Q <= 0 || H <= 0 || cap <= 0 || top_k <= 0 || W <= 0) return CSA2_ERR_INVALID_ARG;
   if (cap % CSA2_BLOCK != 0 || !(scale > 0.f) || !isfinite(scale)) return CSA2_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(swa_kv, 16) || !aligned(out, 16))
-    return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16)) return CSA2_ERR_INVALID_ARG;
   if (H > CSA2_MAX_HEADS) return CSA2_ERR_UNSUPPORTED;
   if ((size_t)cap / CSA2_BLOCK * CSA2_RECORD_BYTES > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
   const size_t need = csa2_attend_layer_ws(B, Q, H, top_k, W);
@@ -262,15 +286,36 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
   p.o_out = o_part; p.lse_out = lse_part; p.out_splits = total;
   p.splits = s_sparse; p.split_base = 0;
   int rc = launch_sparse_fp4(p, st);
-  if (!rc) {
-    AttnParams pw = p;
-    pw.cache = nullptr; pw.idx = nullptr; pw.count = nullptr; pw.n_entries = nullptr;
-    pw.swa = swa_kv; pw.swa_len = swa_len; pw.swa_pos0 = swa_pos0; pw.W = W; pw.Lw = Lw;
-    pw.splits = s_window; pw.split_base = s_sparse;
-    rc = launch_window(pw, st);
-  }
   if (!rc) rc = launch_combine(o_part, lse_part, rows, total, H, nullptr, nullptr, out, lse_out, st);
   return launch_status(rc);
+}
+
+int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
+                      const int32_t* count, const int32_t* n_entries, const int32_t* q_pos,
+                      const uint16_t* swa_kv, const int32_t* swa_len, const int32_t* swa_pos0,
+                      int B, int Q, int H, int cap, int top_k, int W, int Lw, float scale,
+                      float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  // validate both phases before enqueuing either
+  if (!q || !cache || !idx || !count || !n_entries || !swa_kv || !swa_len || !out || !lse_out)
+    return CSA2_ERR_INVALID_ARG;
+  if (B <= 0 || Q <= 0 || H <= 0 || cap <= 0 || top_k <= 0 || W <= 0 || Lw <= 0)
+    return CSA2_ERR_INVALID_ARG;
+  if (cap % CSA2_BLOCK != 0 || !(scale > 0.f) || !isfinite(scale)) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(swa_kv, 16) || !aligned(out, 16))
+    return CSA2_ERR_INVALID_ARG;
+  if (H > CSA2_MAX_HEADS) return CSA2_ERR_UNSUPPORTED;
+  if ((size_t)cap / CSA2_BLOCK * CSA2_RECORD_BYTES > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
+  const size_t need = csa2_attend_layer_ws(B, Q, H, top_k, W);
+  if (!ws || ws_bytes < need) return CSA2_ERR_WS_TOO_SMALL;
+  if (!aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
+  const int rows = B * Q;
+  if (sparse_fp4_splits(rows, H, attn_n_tiles(top_k)) + window_splits(rows, H, (W + 31) / 32) > 128)
+    return CSA2_ERR_UNSUPPORTED;
+  int rc = csa2_attend_layer_window(q, swa_kv, swa_len, swa_pos0, q_pos, B, Q, H, top_k, W, Lw, scale,
+                                    ws, ws_bytes, stream);
+  if (rc != CSA2_OK) return rc;
+  return csa2_attend_layer_sparse(q, cache, idx, count, n_entries, q_pos, B, Q, H, cap, top_k, W, scale,
+                                  out, lse_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

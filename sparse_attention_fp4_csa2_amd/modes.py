@@ -65,6 +65,7 @@ class LayerBuffers:
         self.ws_attn = _ws(_lib.sparse_attn_ws(B, Q, H, top_k), dev)
         self.ws_swa = _ws(_lib.swa_merge_ws(B, Q, H, W), dev)
         self.ws_layer = _ws(_lib.attend_layer_ws(B, Q, H, top_k, W), dev)
+        self.window_done = torch.cuda.Event() if torch.device(dev).type == "cuda" else None
 
 
 def _ws(nbytes, dev):
@@ -98,18 +99,36 @@ def attend(buf, cache, q, swa, swa_len, idx=None, count=None, swa_pos0=None, q_p
                    buf.ws_swa, swa_pos0=swa_pos0, q_pos=q_pos, stream=stream)
 
 
-def run_layer(mode, buf, cache, q, swa, swa_len, q_idx=None, w=None, prev=None, stream=None):
+def run_layer(mode, buf, cache, q, swa, swa_len, q_idx=None, w=None, prev=None, stream=None,
+              side_stream=None):
     """One decode layer.  mode: "F" (Full), "R" (Reindex) or "U" (Reuse, needs ``prev``).
+
+    side_stream: run the window branch there (phase 1 of csa2_attend_layer),
+    forked after the work already on ``stream`` and joined before the sparse
+    branch, so it overlaps the indexer and top-K.  Same results either way.
 
     Returns the (idx, count) this layer attended; for Reuse they are ``prev``'s
     buffers themselves, untouched.
     """
+    if mode not in ("F", "R", "U"):
+        raise ValueError(f"unknown mode {mode!r}")
+    if mode == "U" and prev is None:
+        raise ValueError("Reuse needs the earlier layer's (idx, count)")
+    main = stream if stream is not None else torch.cuda.current_stream()
+    if side_stream is not None:
+        side_stream.wait_stream(main)
+        _lib.attend_layer_window(q, swa, swa_len, buf.top_k, buf.W, SCALE, buf.ws_layer,
+                                 stream=side_stream)
+        buf.window_done.record(side_stream)
     if mode in ("F", "R"):
-        index(buf, cache, q_idx, w, stream=stream)
-        attend(buf, cache, q, swa, swa_len, stream=stream)
-        return buf.idx, buf.count
-    if mode == "U":
+        index(buf, cache, q_idx, w, stream=main)
+        idx, count = buf.idx, buf.count
+    else:
         idx, count = prev
-        attend(buf, cache, q, swa, swa_len, idx=idx, count=count, stream=stream)
-        return idx, count
-    raise ValueError(f"unknown mode {mode!r}")
+    if side_stream is not None:
+        main.wait_event(buf.window_done)
+        _lib.attend_layer_sparse(q, cache.records, idx, count, cache.n_entries, buf.W, SCALE, buf.out,
+                                 buf.lse_out, buf.ws_layer, stream=main)
+    else:
+        attend(buf, cache, q, swa, swa_len, idx=idx, count=count, stream=main)
+    return idx, count

@@ -84,6 +84,21 @@ def test_host_validation_rejects_before_launch(lib):
     assert lib.csa2_swa_merge(fake, fake, fake, None, None, 1, 1, 16, 0, 8, 0.04,
                               fake, fake, fake, fake, fake, 1 << 20, None) == -1
     assert lib.csa2_topk(fake, 1, 70000, 4, fake, fake, None) == -2
+    # one-call layer and its two phases: null window, workspace too small
+    need = lib.csa2_attend_layer_ws(2, 1, 64, 2048, 512)
+    assert need > 0
+    assert lib.csa2_attend_layer(fake, fake, fake, fake, fake, None, None, fake, None, 2, 1, 64, 32768,
+                                 2048, 512, 512, 0.04, fake, fake, fake, need, None) == -1
+    assert lib.csa2_attend_layer(fake, fake, fake, fake, fake, None, fake, fake, None, 2, 1, 64, 32768,
+                                 2048, 512, 512, 0.04, fake, fake, fake, need - 1, None) == -3
+    assert lib.csa2_attend_layer_window(fake, fake, fake, None, None, 2, 1, 64, 2048, 512, 512, 0.04,
+                                        fake, need - 1, None) == -3
+    assert lib.csa2_attend_layer_window(fake, None, fake, None, None, 2, 1, 64, 2048, 512, 512, 0.04,
+                                        fake, need, None) == -1
+    assert lib.csa2_attend_layer_sparse(fake, fake, fake, fake, fake, None, 2, 1, 64, 32768, 2048, 512,
+                                        0.04, fake, fake, fake, need - 1, None) == -3
+    assert lib.csa2_attend_layer_sparse(fake, fake, fake, fake, fake, None, 2, 1, 129, 32768, 2048, 512,
+                                        0.04, fake, fake, fake, need, None) == -2
 
 
 def test_workspace_sizes_are_pure_and_monotone(lib):

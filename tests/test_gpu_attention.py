@@ -328,3 +328,64 @@ def test_attend_layer_causal_rows():
                                   q_pos=int(q_pos[0, r]), swa_pos0=pos0)
         assert_close_rms(out[0, r], ro, what=f"row {r}")
         assert_lse_close(lse[0, r], rl)
+
+
+def test_two_phase_layer_on_two_streams_matches_one_call():
+    # csa2_attend_layer_window on a second stream + csa2_attend_layer_sparse on
+    # the first (joined by an event) gives csa2_attend_layer's bytes exactly;
+    # twice in a row on one workspace, the second call with other queries
+    lib = _lib()
+    rng = rng_for(52)
+    B, Q, H, N, K, W, Lw = 2, 3, 64, 4096, 128, 96, 96
+    latent = normal_bf16(rng, (B, N, 512))
+    cache = gpu_cache(latent, N)
+    swa = normal_bf16(rng, (B, Lw, 512))
+    pos0 = [2 * N - 60, 2 * N - 90]
+    q_pos = np.array([[2 * N - 50, 2 * N - 10, 2 * N + 20], [2 * N - 90, 2 * N - 1, 2 * N + 5]], np.int32)
+    idx = np.stack([np.sort(rng.choice(N // 8, K, replace=False)) for _ in range(B * Q)])
+    idx = idx.reshape(B, Q, K).astype(np.int32)
+    count = np.array([[K, 50, 0], [K, K, 7]], np.int32)
+    n_entries = np.array([N, N - 100], np.int32)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ws = torch.empty(lib.attend_layer_ws(B, Q, H, K, W), dtype=torch.uint8, device="cuda")
+    d_idx, d_cnt, d_n = dev(idx), dev(count), dev(n_entries)
+    d_swa, d_len, d_pos0, d_qpos = dev_bf16(swa), dev(np.array([Lw, Lw], np.int32)), dev(np.array(pos0, np.int32)), dev(q_pos)
+    for call in range(2):
+        q = normal_bf16(rng, (B, Q, H, 512))
+        ref_o, ref_l = gpu_layer(q, cache, idx, count, n_entries, swa, [Lw, Lw], W, swa_pos0=pos0, q_pos=q_pos)
+        d_q = dev_bf16(q)
+        out = torch.full((B, Q, H, 512), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((B, Q, H), float("nan"), dtype=torch.float32, device="cuda")
+        side.wait_stream(main)
+        lib.attend_layer_window(d_q, d_swa, d_len, K, W, SCALE, ws, swa_pos0=d_pos0, q_pos=d_qpos, stream=side)
+        done = torch.cuda.Event()
+        done.record(side)
+        main.wait_event(done)
+        lib.attend_layer_sparse(d_q, cache, d_idx, d_cnt, d_n, W, SCALE, out, lse, ws, q_pos=d_qpos, stream=main)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), ref_o), f"call {call}: out differs from csa2_attend_layer"
+        assert np.array_equal(host(lse), ref_l), f"call {call}: lse differs from csa2_attend_layer"
+
+
+def test_run_layer_side_stream_matches_one_stream():
+    # modes.run_layer with the window branch forked onto a second stream gives
+    # the same bytes as the one-stream call, for a Full and a Reuse layer
+    from sparse_attention_fp4_csa2_amd import modes as gm
+    cfg = CONFIGS["tiny"]
+    x = decode_inputs(cfg)
+    cache = gm.LatentCache.empty(cfg.B, cfg.N)
+    cache.append(dev_bf16(x.latent), dev_bf16(x.keys))
+    q, swa, swa_len = dev_bf16(x.q), dev_bf16(x.swa), dev(np.asarray(x.swa_len, np.int32))
+    qi, w = dev_bf16(x.q_idx), dev(x.w)
+    side = torch.cuda.Stream()
+    res = []
+    for s in (None, side):
+        bf = gm.LayerBuffers(cfg.B, cfg.Q, cfg.H, cfg.N, cfg.K, cfg.W)
+        bu = gm.LayerBuffers(cfg.B, cfg.Q, cfg.H, cfg.N, cfg.K, cfg.W)
+        prev = gm.run_layer("F", bf, cache, q, swa, swa_len, q_idx=qi, w=w, side_stream=s)
+        gm.run_layer("U", bu, cache, q, swa, swa_len, prev=prev, side_stream=s)
+        torch.cuda.synchronize()
+        res.append([host(t) for t in (bf.idx, bf.count, bf.out, bf.lse_out, bu.out, bu.lse_out)])
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
