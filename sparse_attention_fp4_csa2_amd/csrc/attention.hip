@@ -54,8 +54,14 @@ __device__ __forceinline__ floatx16 mfma_bf16(uint4 a, uint4 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16(uint16_t a, uint16_t b) {
-  return (uint32_t)a | ((uint32_t)b << 16);
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// (a, b) -> bf16 hi parts (v_cvt_pk_bf16_f32, round to nearest even) and the
+// bf16 of the remainders, so that hi + lo carries 16 significant bits.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, bf16x2));
+  const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xFFFF0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a - ha, b - hb}, bf16x2));
 }
 
 }  // namespace
@@ -204,14 +210,11 @@ __global__ __launch_bounds__(256, 1) void window_kernel(AttnParams p) {
     uint4 pb[2], pl[2];
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      uint16_t hi[8], lw[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        hi[j] = f32_to_bf16_rne(pr[8 * ks2 + j]);
-        lw[j] = f32_to_bf16_rne(pr[8 * ks2 + j] - bf16_to_f32(hi[j]));
-      }
-      pb[ks2] = make_uint4(pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3]), pack_bf16(hi[4], hi[5]), pack_bf16(hi[6], hi[7]));
-      pl[ks2] = make_uint4(pack_bf16(lw[0], lw[1]), pack_bf16(lw[2], lw[3]), pack_bf16(lw[4], lw[5]), pack_bf16(lw[6], lw[7]));
+      const float* q8 = pr + 8 * ks2;
+      split_bf16x2(q8[0], q8[1], pb[ks2].x, pl[ks2].x);
+      split_bf16x2(q8[2], q8[3], pb[ks2].y, pl[ks2].y);
+      split_bf16x2(q8[4], q8[5], pb[ks2].z, pl[ks2].z);
+      split_bf16x2(q8[6], q8[7], pb[ks2].w, pl[ks2].w);
     }
     // V^T(t) fragments for the P.V MFMAs, read early so their latency hides
     // under the next tile's Q.K work
