@@ -290,12 +290,12 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   // 4hh' + j (j < 4) or 8 + 4hh' + j - 4
   const int pslot = 16 * (dq >> 1) + 8 * hh + 4 * (dq & 1);
 
-  Raw rn;
+  Raw ra, rb;             // raw tiles, alternating: one is consumed, one is in flight
   uint32_t vmask_cur = 0;
   if (t_begin < t_end) {
     Raw r0;
     fetch(t_begin, r0);
-    fetch(t_begin + 1, rn);
+    fetch(t_begin + 1, ra);
     base_v = raise_base(r0, 0);
     base_o = base_v;
     uint4 kf0[8];
@@ -334,14 +334,17 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     *reinterpret_cast<uint2*>(pdst) = make_uint2(pack_f16(pr[0], pr[1]), pack_f16(pr[2], pr[3]));
   };
 
-  // Pipeline, two barriers per tile t:
+  // Pipeline, two barriers per tile t (rc = tile t+1's records, loaded during
+  // tile t-1; rl receives tile t+2's, requested first so that a whole tile of
+  // work hides their latency):
   //   X(t) = [B1(t), B2(t)): P.V(t-1) MFMAs | S(t) quarter reads, softmax,
   //          P(t) written; dequantisation of tile t+1 into registers
   //   Y(t) = [B2(t), B1(t+1)): P^T(t), V^T(t) reads | V(t+1) written, Q.K(t+1)
-  //          MFMAs, S(t+1) partial written; records of tile t+2 requested
-  for (int t = t_begin; t < t_end; ++t) {
+  //          MFMAs, S(t+1) partial written
+  auto tile_step = [&](int t, Raw& rc, Raw& rl) {
     const int buf = t & 1;
     const bool more = t + 1 < t_end;
+    fetch(t + 2, rl);
     // ---- X(t) ---------------------------------------------------------------
     floatx4 sw[4];
 #pragma unroll
@@ -350,8 +353,8 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     uint4 kf[8];
     int base_next = base_v;
     if (more) {
-      base_next = raise_base(rn, base_v);
-      dequant_v(rn, base_next, kf);
+      base_next = raise_base(rc, base_v);
+      dequant_v(rc, base_next, kf);
     }
     floatx4 sq;
 #pragma unroll
@@ -415,12 +418,15 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
 
     if (more) {
       write_v(kf);                // after this wave's V^T(t) reads: the LDS keeps their order
-      qk_s(rn);
-      vmask_cur = (uint32_t)__ballot(rn.valid);
+      qk_s(rc);
+      vmask_cur = (uint32_t)__ballot(rc.valid);
       base_v = base_next;
-      fetch(t + 2, rn);
       __syncthreads();
     }
+  };
+  for (int t = t_begin; t < t_end; t += 2) {
+    tile_step(t, ra, rb);
+    if (t + 1 < t_end) tile_step(t + 1, rb, ra);
   }
   if (have_pv) issue_pv();
 
