@@ -295,7 +295,6 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
                       const uint16_t* swa_kv, const int32_t* swa_len, const int32_t* swa_pos0,
                       int B, int Q, int H, int cap, int top_k, int W, int Lw, float scale,
                       float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
-  // validate both phases before enqueuing either
   if (!q || !cache || !idx || !count || !n_entries || !swa_kv || !swa_len || !out || !lse_out)
     return CSA2_ERR_INVALID_ARG;
   if (B <= 0 || Q <= 0 || H <= 0 || cap <= 0 || top_k <= 0 || W <= 0 || Lw <= 0)
@@ -311,11 +310,30 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
   const int rows = B * Q;
   if (sparse_fp4_splits(rows, H, attn_n_tiles(top_k)) + window_splits(rows, H, (W + 31) / 32) > 128)
     return CSA2_ERR_UNSUPPORTED;
-  int rc = csa2_attend_layer_window(q, swa_kv, swa_len, swa_pos0, q_pos, B, Q, H, top_k, W, Lw, scale,
-                                    ws, ws_bytes, stream);
-  if (rc != CSA2_OK) return rc;
-  return csa2_attend_layer_sparse(q, cache, idx, count, n_entries, q_pos, B, Q, H, cap, top_k, W, scale,
-                                  out, lse_out, ws, ws_bytes, stream);
+  const int s_sparse = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
+  const int s_window = window_splits(rows, H, (W + 31) / 32);
+  const int total = s_sparse + s_window;
+  float* o_part = static_cast<float*>(ws);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                             align_up((size_t)rows * total * H * CSA2_D * sizeof(float)));
+  hipStream_t st = as_stream(stream);
+  // sparse branch -> splits [0, s_sparse); window -> [s_sparse, total); one combine
+  AttnParams p{};
+  p.q = q; p.cache = cache; p.idx = idx; p.count = count; p.n_entries = n_entries;
+  p.top_k = top_k; p.cap = cap; p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.o_out = o_part; p.lse_out = lse_part; p.out_splits = total;
+  p.splits = s_sparse; p.split_base = 0;
+  int rc = launch_sparse_fp4(p, st);
+  if (!rc) {
+    AttnParams pw = p;
+    pw.cache = nullptr; pw.idx = nullptr; pw.count = nullptr; pw.n_entries = nullptr;
+    pw.swa = swa_kv; pw.swa_len = swa_len; pw.swa_pos0 = swa_pos0; pw.W = W; pw.Lw = Lw;
+    pw.splits = s_window; pw.split_base = s_sparse;
+    rc = launch_window(pw, st);
+  }
+  if (!rc) rc = launch_combine(o_part, lse_part, rows, total, H, nullptr, nullptr, out, lse_out, st);
+  return launch_status(rc);
 }
 
 }  // extern "C"
