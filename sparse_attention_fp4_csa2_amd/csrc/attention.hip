@@ -40,7 +40,7 @@ constexpr int VROWU = 20;                // 16-byte units per V row: 16 data + 4
 constexpr int PROW = 40;                 // bf16 slots per P row (32 tokens + 8 pad)
 constexpr float LAZY_LOG2 = 8.0f;        // move the running max only when it grows by > 2^8
 constexpr float M_INIT = -1.0e30f;       // finite "no max yet": exp2(x - M_INIT) never NaN
-constexpr int WINDOW_TARGET_WGS = 512;   // workgroups the split count aims for (two per CU)
+constexpr int WINDOW_TARGET_WGS = 256;   // workgroups the split count aims for
 constexpr int WINDOW_MIN_TILES = 2;      // tiles per split, at least
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
