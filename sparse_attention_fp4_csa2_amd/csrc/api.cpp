@@ -49,6 +49,43 @@ IndexWs index_ws_layout(int B, int Q, int cap, int top_groups) {
 
 int attn_n_tiles(int top_k) { return (top_k + 3) / 4; }
 
+// Split-K partials of the attention calls: fp16 o [rows][splits][H][512],
+// int32 exponent and fp32 lse [rows][splits][H].
+struct PartWs {
+  size_t o16, oexp, lse, total;
+};
+
+PartWs part_ws_layout(int rows, int splits, int H) {
+  const size_t n = (size_t)rows * splits * H;
+  PartWs l{};
+  size_t off = 0;
+  l.o16 = off; off += align_up(n * CSA2_D * sizeof(uint16_t));
+  l.oexp = off; off += align_up(n * sizeof(int32_t));
+  l.lse = off; off += align_up(n * sizeof(float));
+  l.total = off;
+  return l;
+}
+
+// point p's split outputs at the partial buffers in ws
+void set_partials(AttnParams& p, void* ws, const PartWs& l, int out_splits, int split_base) {
+  char* base = static_cast<char*>(ws);
+  p.o_out = nullptr;
+  p.o16_out = reinterpret_cast<uint16_t*>(base + l.o16);
+  p.oexp_out = reinterpret_cast<int32_t*>(base + l.oexp);
+  p.lse_out = reinterpret_cast<float*>(base + l.lse);
+  p.out_splits = out_splits;
+  p.split_base = split_base;
+}
+
+int combine_partials(void* ws, const PartWs& l, int rows, int splits, int H, const float* o_ext,
+                     const float* lse_ext, float* out, float* lse_out, hipStream_t st) {
+  char* base = static_cast<char*>(ws);
+  return launch_combine(reinterpret_cast<const uint16_t*>(base + l.o16),
+                        reinterpret_cast<const int32_t*>(base + l.oexp),
+                        reinterpret_cast<const float*>(base + l.lse), rows, splits, H, o_ext, lse_ext,
+                        out, lse_out, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,8 +181,7 @@ size_t csa2_sparse_attn_ws(int B, int Q, int H, int top_k) {
   const int rows = B * Q;
   const int s = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
   if (s <= 1) return 0;
-  return align_up((size_t)rows * s * H * CSA2_D * sizeof(float)) +
-         align_up((size_t)rows * s * H * sizeof(float));
+  return part_ws_layout(rows, s, H).total;
 }
 
 int csa2_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
@@ -166,19 +202,17 @@ int csa2_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx
   AttnParams p{};
   p.q = q; p.cache = cache; p.idx = idx; p.count = count; p.n_entries = n_entries;
   p.top_k = top_k; p.cap = cap; p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows;
-  p.splits = splits; p.out_splits = splits; p.split_base = 0;
+  p.splits = splits;
   p.scale_log2 = scale * 1.4426950408889634f;
   hipStream_t st = as_stream(stream);
   if (splits == 1) {
-    p.o_out = o; p.lse_out = lse;
+    p.o_out = o; p.lse_out = lse; p.out_splits = 1; p.split_base = 0;
     return launch_status(launch_sparse_fp4(p, st));
   }
-  float* o_part = static_cast<float*>(ws);
-  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                             align_up((size_t)rows * splits * H * CSA2_D * sizeof(float)));
-  p.o_out = o_part; p.lse_out = lse_part;
+  const PartWs l = part_ws_layout(rows, splits, H);
+  set_partials(p, ws, l, splits, 0);
   int rc = launch_sparse_fp4(p, st);
-  if (!rc) rc = launch_combine(o_part, lse_part, rows, splits, H, nullptr, nullptr, o, lse, st);
+  if (!rc) rc = combine_partials(ws, l, rows, splits, H, nullptr, nullptr, o, lse, st);
   return launch_status(rc);
 }
 
@@ -186,8 +220,7 @@ size_t csa2_swa_merge_ws(int B, int Q, int H, int W) {
   if (B <= 0 || Q <= 0 || H <= 0 || W <= 0) return 0;
   const int rows = B * Q;
   const int s = window_splits(rows, H, (W + 31) / 32);
-  return align_up((size_t)rows * s * H * CSA2_D * sizeof(float)) +
-         align_up((size_t)rows * s * H * sizeof(float));
+  return part_ws_layout(rows, s, H).total;
 }
 
 int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa_len,
@@ -209,15 +242,12 @@ int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa
   AttnParams p{};
   p.q = q; p.swa = swa_kv; p.swa_len = swa_len; p.swa_pos0 = swa_pos0; p.W = W; p.Lw = Lw;
   p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows; p.splits = splits;
-  p.out_splits = splits; p.split_base = 0;
   p.scale_log2 = scale * 1.4426950408889634f;
-  float* o_part = static_cast<float*>(ws);
-  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                             align_up((size_t)rows * splits * H * CSA2_D * sizeof(float)));
-  p.o_out = o_part; p.lse_out = lse_part;
+  const PartWs l = part_ws_layout(rows, splits, H);
+  set_partials(p, ws, l, splits, 0);
   hipStream_t st = as_stream(stream);
   int rc = launch_window(p, st);
-  if (!rc) rc = launch_combine(o_part, lse_part, rows, splits, H, o_sparse, lse_sparse, out, lse_out, st);
+  if (!rc) rc = combine_partials(ws, l, rows, splits, H, o_sparse, lse_sparse, out, lse_out, st);
   return launch_status(rc);
 }
 
@@ -225,8 +255,7 @@ size_t csa2_attend_layer_ws(int B, int Q, int H, int top_k, int W) {
   if (B <= 0 || Q <= 0 || H <= 0 || top_k <= 0 || W <= 0) return 0;
   const int rows = B * Q;
   const int total = sparse_fp4_splits(rows, H, attn_n_tiles(top_k)) + window_splits(rows, H, (W + 31) / 32);
-  return align_up((size_t)rows * total * H * CSA2_D * sizeof(float)) +
-         align_up((size_t)rows * total * H * sizeof(float));
+  return part_ws_layout(rows, total, H).total;
 }
 
 int csa2_attend_layer_window(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa_len,
@@ -250,10 +279,8 @@ int csa2_attend_layer_window(const uint16_t* q, const uint16_t* swa_kv, const in
   pw.q = q; pw.swa = swa_kv; pw.swa_len = swa_len; pw.swa_pos0 = swa_pos0; pw.W = W; pw.Lw = Lw;
   pw.q_pos = q_pos; pw.Q = Q; pw.H = H; pw.rows = rows;
   pw.scale_log2 = scale * 1.4426950408889634f;
-  pw.o_out = static_cast<float*>(ws);
-  pw.lse_out = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                        align_up((size_t)rows * total * H * CSA2_D * sizeof(float)));
-  pw.out_splits = total; pw.splits = s_window; pw.split_base = s_sparse;
+  pw.splits = s_window;
+  set_partials(pw, ws, part_ws_layout(rows, total, H), total, s_sparse);
   return launch_status(launch_window(pw, as_stream(stream)));
 }
 
@@ -275,18 +302,16 @@ int csa2_attend_layer_sparse(const uint16_t* q, const uint8_t* cache, const int3
   const int s_window = window_splits(rows, H, (W + 31) / 32);
   const int total = s_sparse + s_window;
   if (total > 128) return CSA2_ERR_UNSUPPORTED;
-  float* o_part = static_cast<float*>(ws);
-  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                             align_up((size_t)rows * total * H * CSA2_D * sizeof(float)));
+  const PartWs l = part_ws_layout(rows, total, H);
   hipStream_t st = as_stream(stream);
   AttnParams p{};
   p.q = q; p.cache = cache; p.idx = idx; p.count = count; p.n_entries = n_entries;
   p.top_k = top_k; p.cap = cap; p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows;
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.o_out = o_part; p.lse_out = lse_part; p.out_splits = total;
-  p.splits = s_sparse; p.split_base = 0;
+  p.splits = s_sparse;
+  set_partials(p, ws, l, total, 0);
   int rc = launch_sparse_fp4(p, st);
-  if (!rc) rc = launch_combine(o_part, lse_part, rows, total, H, nullptr, nullptr, out, lse_out, st);
+  if (!rc) rc = combine_partials(ws, l, rows, total, H, nullptr, nullptr, out, lse_out, st);
   return launch_status(rc);
 }
 
@@ -313,17 +338,15 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
   const int s_sparse = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
   const int s_window = window_splits(rows, H, (W + 31) / 32);
   const int total = s_sparse + s_window;
-  float* o_part = static_cast<float*>(ws);
-  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                             align_up((size_t)rows * total * H * CSA2_D * sizeof(float)));
+  const PartWs l = part_ws_layout(rows, total, H);
   hipStream_t st = as_stream(stream);
   // sparse branch -> splits [0, s_sparse); window -> [s_sparse, total); one combine
   AttnParams p{};
   p.q = q; p.cache = cache; p.idx = idx; p.count = count; p.n_entries = n_entries;
   p.top_k = top_k; p.cap = cap; p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows;
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.o_out = o_part; p.lse_out = lse_part; p.out_splits = total;
-  p.splits = s_sparse; p.split_base = 0;
+  p.splits = s_sparse;
+  set_partials(p, ws, l, total, 0);
   int rc = launch_sparse_fp4(p, st);
   if (!rc) {
     AttnParams pw = p;
@@ -332,7 +355,7 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
     pw.splits = s_window; pw.split_base = s_sparse;
     rc = launch_window(pw, st);
   }
-  if (!rc) rc = launch_combine(o_part, lse_part, rows, total, H, nullptr, nullptr, out, lse_out, st);
+  if (!rc) rc = combine_partials(ws, l, rows, total, H, nullptr, nullptr, out, lse_out, st);
   return launch_status(rc);
 }
 

@@ -54,6 +54,7 @@ struct WinLds {
   float qmax[2][4][32];            // [buffer][wave][head] quarter max of z*log2e
   int flag[2][4];                  // [buffer][wave] quarter needs a max move
   float lsum[4][32];               // epilogue: per-wave softmax denominators
+  int emax[4][32];                 // epilogue: per-wave exponent of the largest |o|
 };
 
 __device__ __forceinline__ floatx16 mfma_bf16(uint4 a, uint4 b, floatx16 c) {
@@ -293,20 +294,28 @@ __global__ __launch_bounds__(256, 2) void window_kernel(AttnParams p, int hgroup
   if (lane < 32) lds.lsum[dq][lane] = lq;
   __syncthreads();
   const float l = (lds.lsum[0][e] + lds.lsum[1][e]) + (lds.lsum[2][e] + lds.lsum[3][e]);
+  const float il = l > 0.f ? 1.f / l : 0.f;
+  const size_t orow = ((size_t)row * p.out_splits + p.split_base + split) * p.H + head;
+  if (head_ok && dq == 0 && hh == 0) {
+    const float lse = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
+    p.lse_out[orow] = lse;
+  }
+  // fp16 partial relative to a per-head power of two: the head's largest |o|
+  // lands in [2^14, 2^15); the 4 waves agree on it through LDS
+  float am = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(oacc[mt][i]));
+  am = pair_max(am * il);
+  constexpr int E_NONE = -100000;
+  if (lane < 32) lds.emax[dq][lane] = am > 0.f ? ilogbf(am) : E_NONE;
+  __syncthreads();
+  int k = max(max(lds.emax[0][e], lds.emax[1][e]), max(lds.emax[2][e], lds.emax[3][e]));
+  if (k == E_NONE) k = 0;
   if (head_ok) {
-    const float il = l > 0.f ? 1.f / l : 0.f;
-    if (dq == 0 && hh == 0) {
-      const float lse = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
-      p.lse_out[((size_t)row * p.out_splits + p.split_base + split) * p.H + head] = lse;
-    }
-    float* dst = p.o_out + (((size_t)row * p.out_splits + p.split_base + split) * p.H + head) * D + 128 * dq + 4 * hh;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<float4*>(dst + 32 * mt + 8 * jj) =
-            make_float4(oacc[mt][4 * jj] * il, oacc[mt][4 * jj + 1] * il, oacc[mt][4 * jj + 2] * il,
-                        oacc[mt][4 * jj + 3] * il);
+    if (dq == 0 && hh == 0) p.oexp_out[orow] = k - 14;
+    store_o16_slice(oacc, il, 14 - k, hh, p.o16_out + orow * D + 128 * dq);
   }
 }
 
@@ -331,12 +340,13 @@ int launch_window(const AttnParams& p, hipStream_t stream) {
 }
 
 // ---- combine -----------------------------------------------------------
-// Log-sum-exp merge of the split-K partials (and an optional extra branch) of
-// one (row, head): wave 0 turns the partials' lse into weights in LDS, then
-// every thread streams its float4 of the 512 dims over all splits.
+// Log-sum-exp merge of the split-K partials (and an optional fp32 extra
+// branch) of one (row, head): wave 0 turns the partials' lse and exponents into
+// weights in LDS, then every thread streams 4 of the 512 dims over the splits.
 constexpr int MAX_COMBINE_SPLITS = 128;
 
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ o_part,
+__global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ o16,
+                                                      const int32_t* __restrict__ oexp,
                                                       const float* __restrict__ lse_part,
                                                       int splits, int H,
                                                       const float* __restrict__ o_ext,
@@ -347,7 +357,8 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   __shared__ float L_sh;
   const int h = blockIdx.x, row = blockIdx.y, t = threadIdx.x;
   const size_t rh = (size_t)row * H + h;
-  const float* lp = lse_part + (size_t)row * splits * H + h;     // split s at lp[s * H]
+  const size_t part0 = (size_t)row * splits * H + h;              // split s at part0 + s * H
+  const float* lp = lse_part + part0;
   if (t < 64) {
     const float le = (o_ext && t == 0) ? lse_ext[rh] : -__builtin_inff();
     float m = le;
@@ -363,31 +374,28 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
     for (int k = 1; k < 64; k <<= 1) sum += __shfl_xor(sum, k, 64);
     const float L = m == -__builtin_inff() ? -__builtin_inff() : m + logf(sum);
     for (int s = t; s < splits; s += 64)
-      wts[s] = L == -__builtin_inff() ? 0.f : expf(lp[(size_t)s * H] - L);
+      wts[s] = L == -__builtin_inff() ? 0.f : ldexpf(expf(lp[(size_t)s * H] - L), oexp[part0 + (size_t)s * H]);
     if (t == 0) {
       wts[splits] = (o_ext && L != -__builtin_inff()) ? expf(le - L) : 0.f;
       L_sh = L;
     }
   }
   __syncthreads();
-  const float4* src = reinterpret_cast<const float4*>(o_part + ((size_t)row * splits * H + h) * D) + t;
-  const size_t stride4 = (size_t)H * D / 4;                      // one split, in float4
+  typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+  const uint2* src = reinterpret_cast<const uint2*>(o16 + part0 * D) + t;
+  const size_t stride = (size_t)H * D / 4;                       // one split, in uint2
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](uint2 v, float wv) {
+    const floatx4 f = __builtin_convertvector(__builtin_bit_cast(halfx4, v), floatx4);
+    acc.x += wv * f[0]; acc.y += wv * f[1]; acc.z += wv * f[2]; acc.w += wv * f[3];
+  };
   int s = 0;
   for (; s + 4 <= splits; s += 4) {
-    const float4 v0 = src[(s + 0) * stride4], v1 = src[(s + 1) * stride4];
-    const float4 v2 = src[(s + 2) * stride4], v3 = src[(s + 3) * stride4];
-    const float w0 = wts[s], w1 = wts[s + 1], w2 = wts[s + 2], w3 = wts[s + 3];
-    acc.x += w0 * v0.x + w1 * v1.x + w2 * v2.x + w3 * v3.x;
-    acc.y += w0 * v0.y + w1 * v1.y + w2 * v2.y + w3 * v3.y;
-    acc.z += w0 * v0.z + w1 * v1.z + w2 * v2.z + w3 * v3.z;
-    acc.w += w0 * v0.w + w1 * v1.w + w2 * v2.w + w3 * v3.w;
+    const uint2 v0 = src[(s + 0) * stride], v1 = src[(s + 1) * stride];
+    const uint2 v2 = src[(s + 2) * stride], v3 = src[(s + 3) * stride];
+    add(v0, wts[s]); add(v1, wts[s + 1]); add(v2, wts[s + 2]); add(v3, wts[s + 3]);
   }
-  for (; s < splits; ++s) {
-    const float4 v = src[s * stride4];
-    const float wv = wts[s];
-    acc.x += wv * v.x; acc.y += wv * v.y; acc.z += wv * v.z; acc.w += wv * v.w;
-  }
+  for (; s < splits; ++s) add(src[s * stride], wts[s]);
   if (o_ext) {
     const float we = wts[splits];
     if (we != 0.f) {
@@ -400,11 +408,11 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   if (t == 0) lse_out[rh] = L_sh;
 }
 
-int launch_combine(const float* o_part, const float* lse_part, int rows, int splits, int H,
-                   const float* o_ext, const float* lse_ext, float* out, float* lse_out,
-                   hipStream_t stream) {
+int launch_combine(const uint16_t* o16, const int32_t* oexp, const float* lse_part, int rows,
+                   int splits, int H, const float* o_ext, const float* lse_ext, float* out,
+                   float* lse_out, hipStream_t stream) {
   dim3 grid(H, rows);
-  combine_kernel<<<grid, 128, 0, stream>>>(o_part, lse_part, splits, H, o_ext, lse_ext, out,
+  combine_kernel<<<grid, 128, 0, stream>>>(o16, oexp, lse_part, splits, H, o_ext, lse_ext, out,
                                            lse_out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

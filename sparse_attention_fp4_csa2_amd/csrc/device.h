@@ -65,4 +65,36 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Store one head's slice of an O^T accumulator as fp16 of acc * f * 2^shift
+// (v_ldexp per value: no intermediate overflow).  Lane (head,
+// hh) holds acc[mt][i] = dim 32mt + 8(i/4) + 4hh + i%4 (relative to dst); the
+// lanes hh = 0 and hh = 1 of a head swap halves (v_permlane32_swap) so that each
+// writes 16 contiguous dims [32mt + 16hh, +16) per mt: 32-byte stores.
+__device__ __forceinline__ void store_o16_slice(const floatx16 (&acc)[4], float f, int shift, int hh,
+                                                uint16_t* dst) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                 f2{ldexpf(acc[mt][2 * k] * f, shift), ldexpf(acc[mt][2 * k + 1] * f, shift)}, h2));
+    // hh = 1 sends its dims 4-7, 12-15 (w[0..3]); hh = 0 sends 16-19, 24-27 (w[4..7])
+    uint32_t x[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t snd = hh ? w[d] : w[4 + d];
+      const auto r = __builtin_amdgcn_permlane32_swap(snd, snd, false, false);
+      x[d] = hh ? r[0] : r[1];
+    }
+    const uint4 a = hh ? make_uint4(x[0], x[1], w[4], w[5]) : make_uint4(w[0], w[1], x[0], x[1]);
+    const uint4 c = hh ? make_uint4(x[2], x[3], w[6], w[7]) : make_uint4(w[2], w[3], x[2], x[3]);
+    uint4* o = reinterpret_cast<uint4*>(dst + 32 * mt + 16 * hh);
+    o[0] = a;
+    o[1] = c;
+  }
+}
+
 }  // namespace csa2

@@ -45,9 +45,14 @@ struct AttnParams {
   const int32_t* q_pos;     // [rows] or null
   int Q, H, rows, splits;
   float scale_log2;         // scale * log2(e)
-  float* o_out;             // [rows][out_splits][H][512] (final o when out_splits == 1)
+  // output: either the final fp32 o (o_out, one split) or split-K partials:
+  // o16_out fp16 [rows][out_splits][H][512] with o = o16 * 2^oexp_out per
+  // (row, split, head), so the partials take half the bytes of fp32
+  float* o_out;             // [rows][H][512] final o, or null
+  uint16_t* o16_out;        // [rows][out_splits][H][512] partial o, or null
+  int32_t* oexp_out;        // [rows][out_splits][H] power-of-two exponent of o16_out
   float* lse_out;           // [rows][out_splits][H]
-  int out_splits;           // split stride of o_out / lse_out (>= split_base + splits)
+  int out_splits;           // split stride of the outputs (>= split_base + splits)
   int split_base;           // this launch writes splits [split_base, split_base + splits)
 };
 
@@ -58,9 +63,10 @@ int launch_window(const AttnParams& p, hipStream_t stream);
 int sparse_fp4_splits(int rows, int H, int n_tiles);
 int launch_sparse_fp4(const AttnParams& p, hipStream_t stream);
 
-// Merge split partials (and an optional extra branch) -> out [rows][H][512], lse [rows][H].
-int launch_combine(const float* o_part, const float* lse_part, int rows, int splits, int H,
-                   const float* o_ext, const float* lse_ext, float* out, float* lse_out,
-                   hipStream_t stream);
+// Merge split partials (fp16 o, exponent, lse; and an optional fp32 extra
+// branch) -> out [rows][H][512], lse [rows][H].
+int launch_combine(const uint16_t* o16, const int32_t* oexp, const float* lse_part, int rows,
+                   int splits, int H, const float* o_ext, const float* lse_ext, float* out,
+                   float* lse_out, hipStream_t stream);
 
 }  // namespace csa2

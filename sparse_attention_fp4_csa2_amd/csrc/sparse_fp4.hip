@@ -57,6 +57,7 @@ struct Lds {
   float qmax[2][4][32];            // [buffer][wave][head] quarter max of z*log2e
   int flag[2][4];                  // [buffer][wave] quarter needs a max move
   float lsum[4][32];               // epilogue: per-wave softmax denominators
+  int emax[4][32];                 // epilogue: per-wave exponent of the largest |o|
   int32_t blk[MAX_SPLIT_BLOCKS];   // this split's selected block ids           8 KB
 };
 
@@ -435,21 +436,43 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   if (lane < 32) lds.lsum[dq][lane] = lq;
   __syncthreads();
   const float l = (lds.lsum[0][e] + lds.lsum[1][e]) + (lds.lsum[2][e] + lds.lsum[3][e]);
-  if (head_ok) {
-    const float il = l > 0.f ? 1.f / l : 0.f;
-    if (dq == 0 && hh == 0) {
-      const float lse = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
-      p.lse_out[((size_t)row * p.out_splits + p.split_base + split) * p.H + head] = lse;
+  const float il = l > 0.f ? 1.f / l : 0.f;
+  if (head_ok && dq == 0 && hh == 0) {
+    const float lse = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
+    p.lse_out[((size_t)row * p.out_splits + p.split_base + split) * p.H + head] = lse;
+  }
+  const size_t orow = ((size_t)row * p.out_splits + p.split_base + split) * p.H + head;
+  if (!p.o16_out) {                  // one split: the final fp32 o
+    if (head_ok) {
+      const float f = ldexpf(il, base_o - VBIAS);
+      float* dst = p.o_out + orow * D + 128 * dq + 4 * hh;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<float4*>(dst + 32 * mt + 8 * jj) =
+              make_float4(oacc[mt][4 * jj] * f, oacc[mt][4 * jj + 1] * f, oacc[mt][4 * jj + 2] * f,
+                          oacc[mt][4 * jj + 3] * f);
     }
-    const float f = ldexpf(il, base_o - VBIAS);
-    float* dst = p.o_out + (((size_t)row * p.out_splits + p.split_base + split) * p.H + head) * D + 128 * dq + 4 * hh;
+    return;
+  }
+  // split-K partial: fp16 o relative to a per-head power of two, so the largest
+  // |o| of the head lands in [2^14, 2^15); the 4 waves (each with its own V base)
+  // agree on it through LDS
+  float am = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<float4*>(dst + 32 * mt + 8 * jj) =
-            make_float4(oacc[mt][4 * jj] * f, oacc[mt][4 * jj + 1] * f, oacc[mt][4 * jj + 2] * f,
-                        oacc[mt][4 * jj + 3] * f);
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(oacc[mt][i]));
+  am = pair_max(am * il);
+  constexpr int E_NONE = -100000;
+  if (lane < 32) lds.emax[dq][lane] = am > 0.f ? ilogbf(am) + base_o - VBIAS : E_NONE;
+  __syncthreads();
+  int k = max(max(lds.emax[0][e], lds.emax[1][e]), max(lds.emax[2][e], lds.emax[3][e]));
+  if (k == E_NONE) k = 0;
+  if (head_ok) {
+    if (dq == 0 && hh == 0) p.oexp_out[orow] = k - 14;
+    store_o16_slice(oacc, il, base_o - VBIAS + 14 - k, hh, p.o16_out + orow * D + 128 * dq);
   }
 }
 
