@@ -19,7 +19,7 @@ namespace csa2 {
 
 namespace {
 
-constexpr int CH_FLAT = 2048;   // entries per workgroup (flat)
+constexpr int CH_FLAT = 512;    // entries per workgroup (flat)
 constexpr int CH_GROUP = 512;   // entries per workgroup (one coarse group)
 constexpr int UNROLL = 4;       // 16-entry tiles in flight per wave
 constexpr int MAX_HI = 16;      // indexer heads (rows of the A operand)
