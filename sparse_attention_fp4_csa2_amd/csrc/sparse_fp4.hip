@@ -36,9 +36,7 @@ namespace csa2 {
 namespace {
 
 constexpr int TILE = 32;                 // entries per tile
-constexpr int VROWU = 20;                // 16-byte units per V row: 16 data + 4 pad
-// unit u of V row r sits at u ^ ((r >> 1) & 3): with 20-unit rows both the
-// row writes (b128) and the transposed reads are free of LDS bank conflicts
+constexpr int VCROWU = 5;                // 16-byte units per V code row: 4 data + 1 pad
 constexpr int PROW = 40;                 // fp16 slots per P row (32 entries + 8 pad)
 constexpr int MAX_SPLIT_BLOCKS = 2048;   // selected block ids one workgroup stages in LDS
 constexpr float LAZY_LOG2 = 8.0f;        // move the running max only when it grows by > 2^8
@@ -52,7 +50,8 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 struct Lds {
   floatx4 sp[4][4][64];            // [wave][quarter][lane] partial S^T          16 KB
-  uint4 v[4][TILE * VROWU];        // [wave][entry * VROWU + unit] fp16 V tile  40 KB
+  uint4 vc[4][TILE * VCROWU];      // [wave][entry * VCROWU + unit] FP4 V codes  10 KB
+  uint16_t vf[4][4][32];           // [wave][group][entry] fp16 scale factors    1 KB
   uint16_t pb[2][32 * PROW];       // [buffer][head * PROW + slot] fp16 P        5 KB
   float qmax[2][4][32];            // [buffer][wave][head] quarter max of z*log2e
   int flag[2][4];                  // [buffer][wave] quarter needs a max move
@@ -72,19 +71,24 @@ __device__ __forceinline__ floatx16 mfma_f16(uint4 a, uint4 b, floatx16 c) {
                                                 __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
 }
 
-// 8 MXFP4 codes -> 8 fp16 values, times the float whose bits are scale_bits.
-__device__ __forceinline__ uint4 dequant8_f16(uint32_t codes, uint32_t scale_bits) {
-  const float sc = __uint_as_float(scale_bits);
-  uint4 r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 0));
-  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 1));
-  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 2));
-  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc, 3));
-  return r;
-}
-
 typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+// 8 E2M1 codes (nibble j = element j) -> fp16, times the fp16 factors f[j]
+__device__ __forceinline__ uint4 codes_to_f16(int codes, halfx8 f) {
+  const halfx2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)codes, 1.f, 0);
+  const halfx2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)codes, 1.f, 1);
+  const halfx2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)codes, 1.f, 2);
+  const halfx2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)codes, 1.f, 3);
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, v0 * halfx2{f[0], f[1]});
+  r.y = __builtin_bit_cast(uint32_t, v1 * halfx2{f[2], f[3]});
+  r.z = __builtin_bit_cast(uint32_t, v2 * halfx2{f[4], f[5]});
+  r.w = __builtin_bit_cast(uint32_t, v3 * halfx2{f[6], f[7]});
+  return r;
+}
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {    // v_cvt_pk_f16_f32, RNE
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, halfx2));
 }
@@ -240,24 +244,22 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     if (__any(smax > cur)) return max(cur, wave_max_int(smax));
     return cur;
   };
-  uint4* const vrow = &lds.v[dq][e * VROWU];
-  int vu[4];
+  // V goes through the wave's LDS tile as FP4 codes (a quarter of the fp16
+  // bytes) plus one fp16 factor 2^(sb - vb + VBIAS - 127) per (entry, 32-dim
+  // group); ds_read_b64_tr_b4 transposes the codes (result lane i, nibble n =
+  // nibble i%16 of the word of lane n of its 16-lane group), and the lane
+  // rescales its 16 values per entry after the E2M1 -> fp16 conversion.
+  uint4* const vcrow = &lds.vc[dq][e * VCROWU];
+  auto write_vc = [&](const Raw& r, int vb) {
+    vcrow[hh] = r.c0;                 // dims 32hh + [0, 32) of the wave's 128
+    vcrow[2 + hh] = r.c1;             // dims 64 + 32hh + [0, 32)
 #pragma unroll
-  for (int u = 0; u < 4; ++u) vu[u] = (4 * hh + u) ^ ((e >> 1) & 3);
-  // V (fp16 relative to base vb) of the lane's 64 dims: 8 fragments of 8 values
-  auto dequant_v = [&](const Raw& r, int vb, uint4 (&kf)[8]) {
-    const uint32_t s8 = r.sc >> (8 * hh);           // byte 0: group 4dq+hh, byte 2: 4dq+2+hh
-    const uint32_t b0 = (uint32_t)max((int)(s8 & 0xFF) - vb + VBIAS, 0) << 23;
-    const uint32_t b1 = (uint32_t)max((int)((s8 >> 16) & 0xFF) - vb + VBIAS, 0) << 23;
-    kf[0] = dequant8_f16(r.c0.x, b0); kf[1] = dequant8_f16(r.c0.y, b0);
-    kf[2] = dequant8_f16(r.c0.z, b0); kf[3] = dequant8_f16(r.c0.w, b0);
-    kf[4] = dequant8_f16(r.c1.x, b1); kf[5] = dequant8_f16(r.c1.y, b1);
-    kf[6] = dequant8_f16(r.c1.z, b1); kf[7] = dequant8_f16(r.c1.w, b1);
-  };
-  // ... into row e of the wave's V tile: units 8s + 4hh + u (u < 4), swizzled
-  auto write_v = [&](const uint4 (&kf)[8]) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) { vrow[vu[u]] = kf[u]; vrow[vu[u] + 8] = kf[4 + u]; }
+    for (int g2 = 0; g2 < 2; ++g2) {  // lane hh writes the factors of groups 2hh, 2hh + 1
+      const int g = 2 * hh + g2;
+      const int x = (int)((r.sc >> (8 * g)) & 0xFF) - vb + VBIAS - 127;   // <= 13
+      const _Float16 f = (_Float16)ldexpf(1.f, x);
+      lds.vf[dq][g][e] = __builtin_bit_cast(uint16_t, f);
+    }
   };
   // Q.K partial S^T over the wave's 128 dims -> LDS
   auto qk_s = [&](const Raw& r) {
@@ -281,15 +283,14 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   float l_lane = 0.f;     // softmax denominator over this lane's quarter entries
   int base_o = 0;         // O^T is in units of 2^(base_o - VBIAS)
   int base_v = 0;         // base of the newest dequantised V tile
-  uint2 vt[2][4][2];      // V^T A fragments of the previous tile, [ks2][mt][half]
+  uint4 va[2][4];         // V^T A fragments (fp16) of the previous tile, [ks2][mt]
   uint4 pfr[2];           // P^T B fragments of the previous tile, [ks2]
   int base_prev = 0;      // base of those V^T fragments
   bool have_pv = false;
 
-  // P slot of entry 8dq + 4hh + r within its 16-entry k-step, matching the
-  // k -> entry order of the transposed V^T reads: k = 8hh' + j holds entry
-  // 4hh' + j (j < 4) or 8 + 4hh' + j - 4
-  const int pslot = 16 * (dq >> 1) + 8 * hh + 4 * (dq & 1);
+  // P slot of entry 8dq + 4hh + r: the V^T fragments hold the entries of a
+  // 16-entry k-step in order (k = 8hh' + j is entry 16ks2 + 8hh' + j)
+  const int pslot = 8 * dq + 4 * hh;
 
   Raw ra, rb;             // raw tiles, alternating: one is consumed, one is in flight
   uint32_t vmask_cur = 0;
@@ -299,9 +300,7 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     fetch(t_begin + 1, ra);
     base_v = raise_base(r0, 0);
     base_o = base_v;
-    uint4 kf0[8];
-    dequant_v(r0, base_v, kf0);
-    write_v(kf0);
+    write_vc(r0, base_v);
     qk_s(r0);
     vmask_cur = (uint32_t)__ballot(r0.valid);
   }
@@ -318,13 +317,16 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const uint4 va = make_uint4(vt[ks2][mt][0].x, vt[ks2][mt][0].y, vt[ks2][mt][1].x, vt[ks2][mt][1].y);
-        oacc[mt] = mfma_f16(va, pfr[ks2], oacc[mt]);
+        oacc[mt] = mfma_f16(va[ks2][mt], pfr[ks2], oacc[mt]);
       }
   };
 
-  const int sl = lane & 15, blk16 = lane >> 4;
-  const int u0 = 2 * (blk16 & 1) + ((sl & 3) >> 1);
+  // transposed code reads: source lane n of each 16-lane group points at entry
+  // 16(n/8) + 8(lane/32) + n%8, the 16 dims 32mt + 16((lane/16) & 1) + [0, 16)
+  const int tr_n = lane & 15;
+  const int tr_entry = 16 * (tr_n >> 3) + 8 * hh + (tr_n & 7);
+  const char* const tr_base = reinterpret_cast<const char*>(&lds.vc[dq][tr_entry * VCROWU]) + 8 * ((lane >> 4) & 1);
+  const _Float16* const fac_base = reinterpret_cast<const _Float16*>(&lds.vf[dq][0][8 * hh]);
   auto read_pfr = [&](int buf) {
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2)
@@ -351,12 +353,8 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) sw[w2] = lds.sp[w2][dq][lane];
     if (have_pv) issue_pv();
-    uint4 kf[8];
     int base_next = base_v;
-    if (more) {
-      base_next = raise_base(rc, base_v);
-      dequant_v(rc, base_next, kf);
-    }
+    if (more) base_next = raise_base(rc, base_v);
     floatx4 sq;
 #pragma unroll
     for (int r = 0; r < 4; ++r) sq[r] = (sw[0][r] + sw[1][r]) + (sw[2][r] + sw[3][r]);
@@ -381,18 +379,12 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     const int4 fl = *reinterpret_cast<const int4*>(&lds.flag[buf][0]);
     read_pfr(buf);
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const int r0 = 16 * ks2 + 4 * (blk16 >> 1) + (sl >> 2);
-      const int x0 = (r0 >> 1) & 3, x1 = ((r0 + 8) >> 1) & 3;
-      const uint16_t* vb0 = reinterpret_cast<const uint16_t*>(&lds.v[dq][r0 * VROWU + (u0 ^ x0)]) + 4 * (sl & 1);
-      const uint16_t* vb1 = reinterpret_cast<const uint16_t*>(&lds.v[dq][(r0 + 8) * VROWU + (u0 ^ x1)]) + 4 * (sl & 1);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        vt[ks2][mt][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                                                      (lds_bf16x4*)(vb0 + 32 * mt)));
-        vt[ks2][mt][1] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                                                      (lds_bf16x4*)(vb1 + 32 * mt)));
-      }
+    for (int mt = 0; mt < 4; ++mt) {
+      const auto c = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i*)(tr_base + 16 * mt));
+      const halfx8 f0 = *reinterpret_cast<const halfx8*>(fac_base + 32 * mt);        // entries 8hh + [0, 8)
+      const halfx8 f1 = *reinterpret_cast<const halfx8*>(fac_base + 32 * mt + 16);   // entries 16 + 8hh + [0, 8)
+      va[0][mt] = codes_to_f16(c[0], f0);
+      va[1][mt] = codes_to_f16(c[1], f1);
     }
     base_prev = base_v;
     have_pv = true;
@@ -418,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     l_lane += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
     if (more) {
-      write_v(kf);                // after this wave's V^T(t) reads: the LDS keeps their order
+      write_vc(rc, base_next);    // after this wave's V^T(t) reads: the LDS keeps their order
       qk_s(rc);
       vmask_cur = (uint32_t)__ballot(rc.valid);
       base_v = base_next;
