@@ -389,3 +389,35 @@ def test_run_layer_side_stream_matches_one_stream():
         res.append([host(t) for t in (bf.idx, bf.count, bf.out, bf.lse_out, bu.out, bu.lse_out)])
     for a, b in zip(*res):
         assert np.array_equal(a, b)
+
+
+def _scale_bf16(bits, k):
+    """bf16 bit patterns times 2^k, exactly (nonzero normals whose exponent stays in range)."""
+    b = np.asarray(bits, np.uint16).astype(np.int32)
+    e = (b >> 7) & 0xFF
+    assert ((e == 0) | ((e + k >= 1) & (e + k <= 254))).all()
+    return np.where(e != 0, b + (k << 7), b).astype(np.uint16)
+
+
+def test_attend_layer_extreme_magnitudes():
+    # values near 2^100 and near 2^-100 in either branch: the split-K partials
+    # (fp16 relative to a per-head power of two) and the combine keep them;
+    # logits stay O(1) by scaling the query the other way
+    rng = rng_for(61)
+    B, H, N, K, W, Lw = 3, 64, 2048, 96, 128, 128
+    lat = normal_bf16(rng, (B, N, 512))
+    q = normal_bf16(rng, (B, 1, H, 512))
+    swa = normal_bf16(rng, (B, Lw, 512))
+    ks = [(100, -100, -60), (-100, 100, -100), (0, 0, 0)]        # (latent, query, window) exponents
+    for b, (kl, kq, kw) in enumerate(ks):
+        lat[b], q[b], swa[b] = _scale_bf16(lat[b], kl), _scale_bf16(q[b], kq), _scale_bf16(swa[b], kw)
+    cache = gpu_cache(lat, N)
+    cache_np = [mxfp4.build_records(lat[b], N) for b in range(B)]
+    idx = np.stack([np.sort(rng.choice(N // 8, K, replace=False)) for _ in range(B)])[:, None].astype(np.int32)
+    count = np.full((B, 1), K, np.int32)
+    out, lse = gpu_layer(q, cache, idx, count, np.full(B, N, np.int32), swa, np.full(B, Lw, np.int32), W)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    for b in range(B):
+        ro, rl = modes.attend_row(q[b, 0], cache_np[b], idx[b, 0], K, N, swa[b], Lw, W)
+        assert_close_rms(out[b, 0], ro, what=f"row {b} (2^{ks[b]})")
+        assert_lse_close(lse[b, 0], rl)
