@@ -12,8 +12,10 @@ as the two contend for HBM and CUs.
 Default workload (--config decode64k): decode at 64K context, 32 sequences, 64
 heads, 32768 MXFP4 entries = 4096 blocks of 8 per sequence, 8 x 64 indexer,
 top-K 2048, window 512; seeded N(0,1) bf16 inputs with planted relevant blocks.
-Other configs (decode1m, layers128k, prefill, tiny) time the same step shape on
-their own workloads.
+Other configs (decode1m, layers128k, prefill, specdec64k, tiny) time the same
+step shape on their own workloads; specdec64k is decode64k's cache with 4 query
+rows per sequence at consecutive positions (a token and 3 drafts verified in
+one pass).
 
 Prints ONE JSON line.  `value` = query rows per second (decode queries/s, or
 prefill tokens/s).  `roofline` covers csa2_sparse_attn (attention kernel + its
@@ -56,7 +58,7 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode64k",
-                    choices=["tiny", "decode64k", "decode1m", "layers128k", "prefill"])
+                    choices=["tiny", "decode64k", "decode1m", "layers128k", "prefill", "specdec64k"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -95,6 +97,9 @@ class DecodeWorkload:
         self.new_lat = _bf(x.latent[:, N - 1:N], device)
         self.new_key = _bf(x.keys[:, N - 1:N], device)
         self.start = torch.full((B,), N - 1, dtype=torch.int32, device=device)
+        # several rows per sequence (draft verification): their raw positions
+        self.q_pos = None if x.q_pos is None else torch.from_numpy(x.q_pos).to(device)
+        self.swa_pos0 = None if x.swa_pos0 is None else torch.from_numpy(x.swa_pos0).to(device)
         self.stream = torch.cuda.current_stream()
 
     def append(self):
@@ -108,7 +113,7 @@ class DecodeWorkload:
         for L in self.layers:
             prev = self.modes.run_layer(L["mode"], L["buf"], self.cache, L["q"], L["swa"],
                                         self.swa_len, q_idx=L["q_idx"], w=L["w"], prev=prev,
-                                        stream=self.stream)
+                                        stream=self.stream, q_pos=self.q_pos, swa_pos0=self.swa_pos0)
 
     def calls(self):
         """name -> (callable, launches per step) for the per-call breakdown."""
@@ -118,21 +123,24 @@ class DecodeWorkload:
         n_index = sum(1 for L in self.layers if L["mode"] in ("F", "R"))
         return {
             "append": (self.append, 1),
-            "index_topk": (lambda: m.index(buf, self.cache, L0["q_idx"], L0["w"], stream=s), n_index),
-            "attend_layer": (lambda: m.attend(buf, self.cache, L0["q"], L0["swa"], self.swa_len, stream=s),
+            "index_topk": (lambda: m.index(buf, self.cache, L0["q_idx"], L0["w"], q_pos=self.q_pos, stream=s),
+                           n_index),
+            "attend_layer": (lambda: m.attend(buf, self.cache, L0["q"], L0["swa"], self.swa_len,
+                                              swa_pos0=self.swa_pos0, q_pos=self.q_pos, stream=s),
                              len(self.layers)),
             # the two branches as separate calls (not part of the step; sparse_attn is the roofline unit)
             "sparse_attn": (self.sparse_attn_call, 0),
             "swa_merge": (lambda: lib.swa_merge(L0["q"], L0["swa"], self.swa_len, self.cfg.W, m.SCALE,
                                                 buf.o, buf.lse, buf.out, buf.lse_out, buf.ws_swa,
-                                                stream=s), 0),
+                                                swa_pos0=self.swa_pos0, q_pos=self.q_pos, stream=s), 0),
         }
 
     def sparse_attn_call(self):
         L0 = self.layers[0]
         buf = L0["buf"]
         self._lib.sparse_attn(L0["q"], self.cache.records, buf.idx, buf.count, self.cache.n_entries,
-                              self.modes.SCALE, buf.o, buf.lse, ws=buf.ws_attn, stream=self.stream)
+                              self.modes.SCALE, buf.o, buf.lse, ws=buf.ws_attn, q_pos=self.q_pos,
+                              stream=self.stream)
 
     def attended_entries(self):
         """Selected visible entries summed over rows, for the first layer's selection."""
@@ -221,7 +229,7 @@ def _bf(a, device):
 
 def make_workload(name, device="cuda"):
     """(cfg, host inputs, workload) for a named config, as bench.py times it."""
-    from synth import CONFIGS, decode_inputs, layers_inputs, prefill_inputs
+    from synth import CONFIGS, decode_inputs, layers_inputs, prefill_inputs, specdec_inputs
     from synth.gen import LayerInputs
     cfg = CONFIGS[name]
     if name == "prefill":
@@ -230,7 +238,7 @@ def make_workload(name, device="cuda"):
     if len(cfg.layers) > 1:
         x, layers = layers_inputs(cfg)
     else:
-        x = decode_inputs(cfg)
+        x = specdec_inputs(cfg) if cfg.Q > 1 else decode_inputs(cfg)
         layers = [LayerInputs("F", x.q, x.q_idx, x.w, x.swa, x.planted)]
     return cfg, (x, layers), DecodeWorkload(cfg, x, layers, device)
 
@@ -349,7 +357,9 @@ def workload_config(cfg, rows):
                 f"({cfg.N // 8} blocks of 8), indexer {cfg.Hi}x64"
                 + (f" two-level ({cfg.top_groups} of {cfg.cap // 512} groups)" if cfg.top_groups else "")
                 + f", top-K {cfg.K}, window {cfg.W}"
-                + (f", layers {'/'.join(cfg.layers)}" if len(cfg.layers) > 1 else ""))
+                + (f", layers {'/'.join(cfg.layers)}" if len(cfg.layers) > 1 else "")
+                + (f", {cfg.Q} rows per sequence (1 + {cfg.Q - 1} drafts verified together)"
+                   if cfg.Q > 1 else ""))
     return {"workload": desc, "global_batch": rows, "seq_len": 2 * cfg.N, "parallelism": "single GPU"}
 
 
@@ -427,21 +437,25 @@ def cpu_baseline(cfg, host_in, budget_s):
         what = "index + top-K + attention + window merge per query token, causal"
     else:
         x, layers = host_in
-        total = x.latent.shape[0]
-        for b in range(total):
+        rows = [(b, r) for b in range(x.latent.shape[0]) for r in range(cfg.Q)]
+        total = len(rows)
+        for b, r in rows:
+            qp = None if x.q_pos is None else int(x.q_pos[b, r])
+            p0 = 0 if x.swa_pos0 is None else int(x.swa_pos0[b])
             prev = None
             for L in layers:
                 if L.mode in ("F", "R"):
                     t = time.perf_counter()
-                    idx, cnt = om.select_blocks(L.q_idx[b, 0], L.w[b, 0], x.keys[b], int(x.n_entries[b]),
-                                                cfg.K, top_groups=cfg.top_groups or None, n_blocks=nb)
+                    idx, cnt = om.select_blocks(L.q_idx[b, r], L.w[b, r], x.keys[b], int(x.n_entries[b]),
+                                                cfg.K, q_pos=qp, top_groups=cfg.top_groups or None,
+                                                n_blocks=nb)
                     elapsed += time.perf_counter() - t
                 else:
                     idx, cnt = prev
                 rec = _oracle_records(x.latent[b], idx[:cnt], nb)
                 t = time.perf_counter()
-                om.attend_row(L.q[b, 0], rec, idx, cnt, int(x.n_entries[b]), L.swa[b], int(x.swa_len[b]),
-                              cfg.W)
+                om.attend_row(L.q[b, r], rec, idx, cnt, int(x.n_entries[b]), L.swa[b], int(x.swa_len[b]),
+                              cfg.W, q_pos=qp, swa_pos0=p0)
                 elapsed += time.perf_counter() - t
                 prev = (idx, cnt)
             done += 1

@@ -100,8 +100,12 @@ def attend(buf, cache, q, swa, swa_len, idx=None, count=None, swa_pos0=None, q_p
 
 
 def run_layer(mode, buf, cache, q, swa, swa_len, q_idx=None, w=None, prev=None, stream=None,
-              side_stream=None):
+              side_stream=None, q_pos=None, swa_pos0=None):
     """One decode layer.  mode: "F" (Full), "R" (Reindex) or "U" (Reuse, needs ``prev``).
+
+    q_pos / swa_pos0: raw positions of the query rows and of window slot 0
+    (several rows per sequence, e.g. draft tokens verified together); None =
+    every row is the newest token.
 
     side_stream: run the window branch there (phase 1 of csa2_attend_layer),
     forked after the work already on ``stream`` and joined before the sparse
@@ -118,17 +122,18 @@ def run_layer(mode, buf, cache, q, swa, swa_len, q_idx=None, w=None, prev=None, 
     if side_stream is not None:
         side_stream.wait_stream(main)
         _lib.attend_layer_window(q, swa, swa_len, buf.top_k, buf.W, SCALE, buf.ws_layer,
-                                 stream=side_stream)
+                                 swa_pos0=swa_pos0, q_pos=q_pos, stream=side_stream)
         buf.window_done.record(side_stream)
     if mode in ("F", "R"):
-        index(buf, cache, q_idx, w, stream=main)
+        index(buf, cache, q_idx, w, q_pos=q_pos, stream=main)
         idx, count = buf.idx, buf.count
     else:
         idx, count = prev
     if side_stream is not None:
         main.wait_event(buf.window_done)
         _lib.attend_layer_sparse(q, cache.records, idx, count, cache.n_entries, buf.W, SCALE, buf.out,
-                                 buf.lse_out, buf.ws_layer, stream=main)
+                                 buf.lse_out, buf.ws_layer, q_pos=q_pos, stream=main)
     else:
-        attend(buf, cache, q, swa, swa_len, idx=idx, count=count, stream=main)
+        attend(buf, cache, q, swa, swa_len, idx=idx, count=count, swa_pos0=swa_pos0, q_pos=q_pos,
+               stream=main)
     return idx, count

@@ -16,6 +16,7 @@ at the sizes of the five workloads below):
             two-level indexer keeping 256 groups of 64 blocks
   layers128k B 64, H 64, 65536 entries, 4 layers Full/Reindex/Reuse/Reuse
   prefill   4096 query tokens after 131072 raw positions, H 64, K 2048, W 512
+  specdec64k decode64k's cache with 4 query rows per sequence (1 + 3 drafts)
 """
 
 from .gen import *  # noqa: F401,F403

@@ -37,4 +37,6 @@ CONFIGS = {
                          layers="FRUU", seed=1003),
     "prefill": Config("prefill", B=1, Q=4096, H=64, N=67584, Hi=8, K=2048, W=512,
                       prior=65536, seed=1004),
+    # decode with 3 draft tokens verified in the same pass: 4 query rows per sequence
+    "specdec64k": Config("specdec64k", B=32, Q=4, H=64, N=32768, Hi=8, K=2048, W=512, seed=1005),
 }

@@ -19,6 +19,7 @@ __all__ = [
     "rng_for", "bf16_rne", "bf16_to_f32", "normal_bf16", "DecodeInputs",
     "decode_inputs", "choose_blocks", "plant_dominant", "plant_tight",
     "plant_groups", "layer_query", "prefill_inputs", "LayerInputs", "layers_inputs",
+    "specdec_inputs",
 ]
 
 D = 512
@@ -88,6 +89,8 @@ class DecodeInputs:
     swa_len: np.ndarray     # i32 [B]
     n_entries: np.ndarray   # i32 [B]
     planted: list = field(default_factory=list)   # per sequence: planted block ids
+    q_pos: np.ndarray = None     # i32 [B][Q] raw position of each query row (None: newest)
+    swa_pos0: np.ndarray = None  # i32 [B] raw position of window slot 0 (None: 0)
 
 
 def choose_blocks(rng, nb_present, count, exclude=None, pool=None):
@@ -207,6 +210,34 @@ def decode_inputs(cfg, seed=None, plant="dominant", score_fn=None, n_entries=Non
             raise ValueError(plant)
         planted.append(blocks)
     return DecodeInputs(latent, keys, q, q_idx, w, swa, swa_len, ne, planted)
+
+
+def specdec_inputs(cfg, seed=None, c=3.0, jitter=0.05):
+    """Decode with draft verification: Q = 1 + drafts query rows per sequence.
+
+    The rows sit at raw positions 2N .. 2N + Q - 1 (the tokens after the cached
+    ones; every cached entry is visible to all of them).  Row 0 is drawn and
+    planted as in decode_inputs; the draft rows' indexer queries are row 0's
+    plus N(0, jitter^2) noise and share its weights (neighbouring tokens ask for
+    much the same context), so the plant stands for every row.  The window holds
+    raw positions [2N - W + 1, 2N + Q - 1], the drafts included, so each row
+    sees exactly W window tokens.
+    """
+    x = decode_inputs(cfg, seed=seed, c=c)
+    rng = rng_for((cfg.seed if seed is None else seed) + 104729)
+    B, Q, N, W = x.q.shape[0], cfg.Q, cfg.N, cfg.W
+    q_idx, w = x.q_idx.copy(), x.w.copy()
+    base = bf16_to_f32(q_idx[:, 0])
+    for r in range(1, Q):
+        noise = rng.standard_normal(base.shape, dtype=np.float32) * np.float32(jitter)
+        q_idx[:, r] = bf16_rne(base + noise)
+        w[:, r] = w[:, 0]
+    swa = np.concatenate([x.swa, normal_bf16(rng, (B, Q - 1, D))], axis=1)
+    swa_len = np.full(B, W + Q - 1, dtype=np.int32)
+    q_pos = np.broadcast_to(2 * N + np.arange(Q, dtype=np.int32), (B, Q)).copy()
+    swa_pos0 = np.full(B, 2 * N - W + 1, dtype=np.int32)
+    return DecodeInputs(x.latent, x.keys, x.q, q_idx, w, swa, swa_len, x.n_entries, x.planted,
+                        q_pos=q_pos, swa_pos0=swa_pos0)
 
 
 def prefill_inputs(cfg, seed=None, q_rows=None, n_dirs=4, c=3.0, beta=1.0):

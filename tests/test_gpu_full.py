@@ -70,25 +70,31 @@ def _check_selection(got_idx, got_cnt, scores, k, what, cand_mask=None):
 
 
 def _decode_checks(cfg, x, layers, wl, rows):
+    """rows: sequences to check; every query row of each (cfg.Q per sequence)."""
     nb = cfg.cap // 8
     N = cfg.N
+    Q = cfg.Q
+    qpos = (lambda b, r: None) if x.q_pos is None else (lambda b, r: int(x.q_pos[b, r]))
+    p0 = (lambda b: 0) if x.swa_pos0 is None else (lambda b: int(x.swa_pos0[b]))
     prev_sel = prev_buf = None
     exact = 0
     for li, (L, D) in enumerate(zip(layers, wl.layers)):
         buf = D["buf"]
-        idx, cnt = host(buf.idx)[:, 0], host(buf.count)[:, 0]
-        out, lse = host(buf.out)[:, 0], host(buf.lse_out)[:, 0]
+        idx, cnt = host(buf.idx), host(buf.count)            # [B][Q][K], [B][Q]
+        out, lse = host(buf.out), host(buf.lse_out)
         if L.mode in ("F", "R"):
             for b in range(x.latent.shape[0]):
-                s = indexer.block_scores(L.q_idx[b, 0], L.w[b, 0], x.keys[b], N, n_blocks=nb)
-                mask = None
-                if cfg.top_groups:
-                    gs = indexer.group_scores(L.q_idx[b, 0], L.w[b, 0], x.keys[b], N, n_groups=nb // 64)
-                    assert topk.gap_at_rank(gs, cfg.top_groups) >= GAP, "generator gap at the group rank"
-                    gsel, gc = topk.select(gs, cfg.top_groups)
-                    mask = np.zeros(nb, dtype=bool)
-                    mask[indexer.blocks_of_groups(gsel[:gc])] = True
-                exact += _check_selection(idx[b], int(cnt[b]), s, cfg.K, f"layer {li} row {b}", mask)
+                for r in range(Q):
+                    s = indexer.block_scores(L.q_idx[b, r], L.w[b, r], x.keys[b], N, q_pos=qpos(b, r),
+                                             n_blocks=nb)
+                    mask = None
+                    if cfg.top_groups:
+                        gs = indexer.group_scores(L.q_idx[b, r], L.w[b, r], x.keys[b], N, n_groups=nb // 64)
+                        assert topk.gap_at_rank(gs, cfg.top_groups) >= GAP, "generator gap at the group rank"
+                        gsel, gc = topk.select(gs, cfg.top_groups)
+                        mask = np.zeros(nb, dtype=bool)
+                        mask[indexer.blocks_of_groups(gsel[:gc])] = True
+                    exact += _check_selection(idx[b, r], int(cnt[b, r]), s, cfg.K, f"layer {li} row {b}.{r}", mask)
             sel = (idx, cnt)
             buf_used = buf
         else:
@@ -96,17 +102,17 @@ def _decode_checks(cfg, x, layers, wl, rows):
             # idx/count buffers stay unused); they must still hold what was checked
             assert prev_sel is not None
             src = prev_buf
-            same = (np.array_equal(host(src.idx)[:, 0], prev_sel[0])
-                    and np.array_equal(host(src.count)[:, 0], prev_sel[1]))
+            same = np.array_equal(host(src.idx), prev_sel[0]) and np.array_equal(host(src.count), prev_sel[1])
             assert same, "Reuse layer changed the index buffer it was given"
             sel = prev_sel
             buf_used = src
         ref_o, ref_l, got_o, got_l = [], [], [], []
         for b in rows:
-            rec = _records_of(x.latent[b], sel[0][b, :sel[1][b]], nb)
-            ro, rl = om.attend_row(L.q[b, 0], rec, sel[0][b], int(sel[1][b]), N, L.swa[b],
-                                   int(x.swa_len[b]), cfg.W)
-            ref_o.append(ro), ref_l.append(rl), got_o.append(out[b]), got_l.append(lse[b])
+            for r in range(Q):
+                rec = _records_of(x.latent[b], sel[0][b, r, :sel[1][b, r]], nb)
+                ro, rl = om.attend_row(L.q[b, r], rec, sel[0][b, r], int(sel[1][b, r]), N, L.swa[b],
+                                       int(x.swa_len[b]), cfg.W, q_pos=qpos(b, r), swa_pos0=p0(b))
+                ref_o.append(ro), ref_l.append(rl), got_o.append(out[b, r]), got_l.append(lse[b, r])
         assert_close_rms(np.stack(got_o), np.stack(ref_o), what=f"{cfg.name} layer {li} ({L.mode}) out")
         assert_lse_close(np.stack(got_l), np.stack(ref_l))
         prev_sel = sel
@@ -116,7 +122,7 @@ def _decode_checks(cfg, x, layers, wl, rows):
     rec_gpu = wl.cache.records
     rng = np.random.default_rng(5)
     for b in rows[:4]:
-        blocks = np.unique(np.concatenate([[(N - 1) // 8], rng.choice(prev_sel[0][b, :prev_sel[1][b]], 8)]))
+        blocks = np.unique(np.concatenate([[(N - 1) // 8], rng.choice(prev_sel[0][b, 0, :prev_sel[1][b, 0]], 8)]))
         ref = _records_of(x.latent[b], blocks, nb)
         got = host(rec_gpu[b, torch.from_numpy(blocks).cuda()])
         assert np.array_equal(got, ref[blocks]), f"row {b}: record bytes differ"
@@ -139,6 +145,14 @@ def test_layers128k_full_reindex_reuse():
     cfg, (x, layers), wl = _workload("layers128k")
     rows = sorted(set([0, cfg.B - 1] + list(np.random.default_rng(3).choice(cfg.B, 6, replace=False))))
     _decode_checks(cfg, x, layers, wl, rows=rows)
+
+
+@pytest.mark.timeout(600)
+def test_specdec64k_draft_rows_full_size():
+    # 4 rows per sequence at consecutive positions (a token and 3 drafts), each
+    # with its own selection, causal window and attention
+    cfg, (x, layers), wl = _workload("specdec64k")
+    _decode_checks(cfg, x, layers, wl, rows=list(range(0, cfg.B, 4)))
 
 
 @pytest.mark.timeout(600)

@@ -71,3 +71,24 @@ def test_prefill_generator_shapes_and_gap_on_sample_rows():
         s = indexer.block_scores(x["q_idx"][0, r], x["w"][0, r], x["keys"][0], 4096 + 32,
                                  q_pos=int(x["q_pos"][0, r]))
         assert topk.gap_at_rank(s, 32) >= 1e-2
+
+
+def test_specdec_rows_positions_window_and_plants():
+    # draft rows: consecutive raw positions after the cache, a window that holds
+    # exactly W tokens for each row, and row 0's plant still the top-K of every row
+    from oracle import indexer, topk
+    from synth import specdec_inputs
+    from synth.configs import Config
+    cfg = Config("t", B=2, Q=4, H=16, N=2048, Hi=4, K=32, W=128, seed=7)
+    x = specdec_inputs(cfg)
+    assert (x.q_pos == 2 * cfg.N + np.arange(cfg.Q)).all()
+    assert (x.swa_len == cfg.W + cfg.Q - 1).all() and x.swa.shape[1] == cfg.W + cfg.Q - 1
+    for b in range(cfg.B):
+        for r in range(cfg.Q):
+            t = int(x.q_pos[b, r])
+            lo, hi = max(t - cfg.W + 1, int(x.swa_pos0[b])), min(t, int(x.swa_pos0[b]) + int(x.swa_len[b]) - 1)
+            assert hi - lo + 1 == cfg.W
+            s = indexer.block_scores(x.q_idx[b, r], x.w[b, r], x.keys[b], cfg.N, q_pos=t, n_blocks=cfg.nb)
+            assert topk.gap_at_rank(s, cfg.K) >= 1e-2
+            sel, c = topk.select(s, cfg.K)
+            assert c == cfg.K and np.array_equal(sel, np.sort(x.planted[b]))
