@@ -49,9 +49,9 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 struct Lds {
-  floatx4 sp[4][4][64];            // [wave][quarter][lane] partial S^T          16 KB
-  uint4 vc[4][TILE * VCROWU];      // [wave][entry * VCROWU + unit] FP4 V codes  10 KB
-  uint16_t vf[4][4][32];           // [wave][group][entry] fp16 scale factors    1 KB
+  floatx4 sp[2][4][4][64];         // [buffer][wave][quarter][lane] partial S^T  32 KB
+  uint4 vc[2][4][TILE * VCROWU];   // [buffer][wave][entry * VCROWU + unit] V    20 KB
+  uint16_t vf[2][4][4][32];        // [buffer][wave][group][entry] fp16 factors   2 KB
   uint16_t pb[2][32 * PROW];       // [buffer][head * PROW + slot] fp16 P        5 KB
   float qmax[2][4][32];            // [buffer][wave][head] quarter max of z*log2e
   int flag[2][4];                  // [buffer][wave] quarter needs a max move
@@ -249,8 +249,8 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   // group); ds_read_b64_tr_b4 transposes the codes (result lane i, nibble n =
   // nibble i%16 of the word of lane n of its 16-lane group), and the lane
   // rescales its 16 values per entry after the E2M1 -> fp16 conversion.
-  uint4* const vcrow = &lds.vc[dq][e * VCROWU];
-  auto write_vc = [&](const Raw& r, int vb) {
+  auto write_vc = [&](int vbuf, const Raw& r, int vb) {
+    uint4* const vcrow = &lds.vc[vbuf][dq][e * VCROWU];
     vcrow[hh] = r.c0;                 // dims 32hh + [0, 32) of the wave's 128
     vcrow[2 + hh] = r.c1;             // dims 64 + 32hh + [0, 32)
 #pragma unroll
@@ -258,11 +258,11 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
       const int g = 2 * hh + g2;
       const int x = (int)((r.sc >> (8 * g)) & 0xFF) - vb + VBIAS - 127;   // <= 13
       const _Float16 f = (_Float16)ldexpf(1.f, x);
-      lds.vf[dq][g][e] = __builtin_bit_cast(uint16_t, f);
+      lds.vf[vbuf][dq][g][e] = __builtin_bit_cast(uint16_t, f);
     }
   };
   // Q.K partial S^T over the wave's 128 dims -> LDS
-  auto qk_s = [&](const Raw& r) {
+  auto qk_s = [&](int sbuf, const Raw& r) {
     // the MFMA reads the E8M0 scale from byte 0 of its scale operand
     const uint32_t s8 = r.sc >> (8 * hh);
     const uint32_t s8b = s8 >> 16;
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     sacc = mfma_fp4_fp8(r.c1, qlo[1], sacc, s8b, qsb_lo);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      lds.sp[dq][j][lane] = floatx4{sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3]};
+      lds.sp[sbuf][dq][j][lane] = floatx4{sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3]};
   };
 
   floatx16 oacc[4];       // O^T: [dims 128dq + 32mt + 8(i/4) + 4hh + i%4][head]
@@ -284,9 +284,10 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   int base_o = 0;         // O^T is in units of 2^(base_o - VBIAS)
   int base_v = 0;         // base of the newest dequantised V tile
   uint4 va[2][4];         // V^T A fragments (fp16) of the previous tile, [ks2][mt]
+  floatx4 sq_prev = floatx4{};   // the previous tile's logits quarter (for a late max move)
+  float pr_prev[4] = {0.f, 0.f, 0.f, 0.f};   // ... and its softmax weights
   uint4 pfr[2];           // P^T B fragments of the previous tile, [ks2]
   int base_prev = 0;      // base of those V^T fragments
-  bool have_pv = false;
 
   // P slot of entry 8dq + 4hh + r: the V^T fragments hold the entries of a
   // 16-entry k-step in order (k = 8hh' + j is entry 16ks2 + 8hh' + j)
@@ -300,8 +301,8 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     fetch(t_begin + 1, ra);
     base_v = raise_base(r0, 0);
     base_o = base_v;
-    write_vc(r0, base_v);
-    qk_s(r0);
+    write_vc(t_begin & 1, r0, base_v);
+    qk_s(t_begin & 1, r0);
     vmask_cur = (uint32_t)__ballot(r0.valid);
   }
   __syncthreads();
@@ -325,8 +326,19 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   // 16(n/8) + 8(lane/32) + n%8, the 16 dims 32mt + 16((lane/16) & 1) + [0, 16)
   const int tr_n = lane & 15;
   const int tr_entry = 16 * (tr_n >> 3) + 8 * hh + (tr_n & 7);
-  const char* const tr_base = reinterpret_cast<const char*>(&lds.vc[dq][tr_entry * VCROWU]) + 8 * ((lane >> 4) & 1);
-  const _Float16* const fac_base = reinterpret_cast<const _Float16*>(&lds.vf[dq][0][8 * hh]);
+  auto read_vt = [&](int vbuf) {
+    const char* const tr_base =
+        reinterpret_cast<const char*>(&lds.vc[vbuf][dq][tr_entry * VCROWU]) + 8 * ((lane >> 4) & 1);
+    const _Float16* const fac_base = reinterpret_cast<const _Float16*>(&lds.vf[vbuf][dq][0][8 * hh]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const auto c = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i*)(tr_base + 16 * mt));
+      const halfx8 f0 = *reinterpret_cast<const halfx8*>(fac_base + 32 * mt);        // entries 8hh + [0, 8)
+      const halfx8 f1 = *reinterpret_cast<const halfx8*>(fac_base + 32 * mt + 16);   // entries 16 + 8hh + [0, 8)
+      va[0][mt] = codes_to_f16(c[0], f0);
+      va[1][mt] = codes_to_f16(c[1], f1);
+    }
+  };
   auto read_pfr = [&](int buf) {
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2)
@@ -336,23 +348,48 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     uint16_t* pdst = &lds.pb[buf][e * PROW + pslot];
     *reinterpret_cast<uint2*>(pdst) = make_uint2(pack_f16(pr[0], pr[1]), pack_f16(pr[2], pr[3]));
   };
+  // Tile t-1's P(t-1).V(t-1), after the rare max move it may need (decided from
+  // every wave's quarter maxima of that tile, visible since the last barrier).
+  auto finish_prev = [&](int pbuf) {
+    const int4 fl = *reinterpret_cast<const int4*>(&lds.flag[pbuf][0]);
+    read_pfr(pbuf);
+    read_vt(pbuf);
+    if (fl.x | fl.y | fl.z | fl.w) {          // rare (always after the first tile)
+      const float tmax = fmaxf(fmaxf(lds.qmax[pbuf][0][e], lds.qmax[pbuf][1][e]),
+                               fmaxf(lds.qmax[pbuf][2][e], lds.qmax[pbuf][3][e]));
+      const float m_new = tmax > m_run + LAZY_LOG2 ? tmax : m_run;
+      if (__any(m_new != m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) oacc[mt] *= alpha;
+        l_lane *= alpha;
+        m_run = m_new;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr_prev[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq_prev[r], c_log2, -m_run));
+      write_p(pbuf, pr_prev);
+      __syncthreads();
+      read_pfr(pbuf);
+    }
+    l_lane += (pr_prev[0] + pr_prev[1]) + (pr_prev[2] + pr_prev[3]);
+    issue_pv();
+  };
 
-  // Pipeline, two barriers per tile t (rc = tile t+1's records, loaded during
-  // tile t-1; rl receives tile t+2's, requested first so that a whole tile of
-  // work hides their latency):
-  //   X(t) = [B1(t), B2(t)): P.V(t-1) MFMAs | S(t) quarter reads, softmax,
-  //          P(t) written; dequantisation of tile t+1 into registers
-  //   Y(t) = [B2(t), B1(t+1)): P^T(t), V^T(t) reads | V(t+1) written, Q.K(t+1)
-  //          MFMAs, S(t+1) partial written
+  // Pipeline, one barrier per tile.  Tile t, between barriers B(t-1) and B(t)
+  // (rc = tile t+1's records, loaded during tile t-1; rl receives tile t+2's,
+  // requested first so that a whole tile of work hides their latency):
+  //   reads: S(t) partials, P(t-1), flags(t-1), V^T(t-1) (all written before B(t-1))
+  //   P(t-1).V(t-1) (after a rare max move) | softmax(t): P(t), flags(t) written
+  //   V(t+1) written, Q.K(t+1), S(t+1) partial written
+  // S, P, flags and the V tile are double-buffered by tile parity.
   auto tile_step = [&](int t, Raw& rc, Raw& rl) {
     const int buf = t & 1;
     const bool more = t + 1 < t_end;
     fetch(t + 2, rl);
-    // ---- X(t) ---------------------------------------------------------------
     floatx4 sw[4];
 #pragma unroll
-    for (int w2 = 0; w2 < 4; ++w2) sw[w2] = lds.sp[w2][dq][lane];
-    if (have_pv) issue_pv();
+    for (int w2 = 0; w2 < 4; ++w2) sw[w2] = lds.sp[buf][w2][dq][lane];
+    if (t > t_begin) finish_prev(buf ^ 1);
     int base_next = base_v;
     if (more) base_next = raise_base(rc, base_v);
     floatx4 sq;
@@ -366,62 +403,27 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     }
     const float hmax = pair_max(fmaxf(fmaxf(sq[0], sq[1]), fmaxf(sq[2], sq[3]))) * c_log2;
     const bool bump = hmax > m_run + LAZY_LOG2;
-    float pr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[r], c_log2, -m_run));
-    write_p(buf, pr);
+    for (int r = 0; r < 4; ++r) pr_prev[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[r], c_log2, -m_run));
+    write_p(buf, pr_prev);
     const int any_bump = __any(bump) ? 1 : 0;
     if (lane < 32) lds.qmax[buf][dq][lane] = hmax;
     if (lane == 0) lds.flag[buf][dq] = any_bump;
-    __syncthreads();
-
-    // ---- Y(t): every LDS read of the tile at once: flags, P^T(t), V^T(t) ------
-    const int4 fl = *reinterpret_cast<const int4*>(&lds.flag[buf][0]);
-    read_pfr(buf);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const auto c = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i*)(tr_base + 16 * mt));
-      const halfx8 f0 = *reinterpret_cast<const halfx8*>(fac_base + 32 * mt);        // entries 8hh + [0, 8)
-      const halfx8 f1 = *reinterpret_cast<const halfx8*>(fac_base + 32 * mt + 16);   // entries 16 + 8hh + [0, 8)
-      va[0][mt] = codes_to_f16(c[0], f0);
-      va[1][mt] = codes_to_f16(c[1], f1);
-    }
-    base_prev = base_v;
-    have_pv = true;
-
-    // rare: a head's max moved by more than 2^8 (always on the first tile)
-    if (fl.x | fl.y | fl.z | fl.w) {
-      const float tmax = fmaxf(fmaxf(lds.qmax[buf][0][e], lds.qmax[buf][1][e]),
-                               fmaxf(lds.qmax[buf][2][e], lds.qmax[buf][3][e]));
-      const float m_new = tmax > m_run + LAZY_LOG2 ? tmax : m_run;
-      if (__any(m_new != m_run)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) oacc[mt] *= alpha;
-        l_lane *= alpha;
-        m_run = m_new;
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[r], c_log2, -m_run));
-      write_p(buf, pr);
-      __syncthreads();
-      read_pfr(buf);
-    }
-    l_lane += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-
+    sq_prev = sq;
+    base_prev = base_v;           // the base tile t's V was written with
     if (more) {
-      write_vc(rc, base_next);    // after this wave's V^T(t) reads: the LDS keeps their order
-      qk_s(rc);
+      write_vc(buf ^ 1, rc, base_next);
+      qk_s(buf ^ 1, rc);
       vmask_cur = (uint32_t)__ballot(rc.valid);
       base_v = base_next;
-      __syncthreads();
     }
+    __syncthreads();
   };
   for (int t = t_begin; t < t_end; t += 2) {
     tile_step(t, ra, rb);
     if (t + 1 < t_end) tile_step(t + 1, rb, ra);
   }
-  if (have_pv) issue_pv();
+  if (t_begin < t_end) finish_prev((t_end - 1) & 1);
 
   // ---- finalize: denominators across the 4 quarter owners -----------------
   const float lq = pair_sum(l_lane);
