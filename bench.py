@@ -327,6 +327,7 @@ def main():
         "fp4_kv_read_TBps": round(kv_tbps, 3),
         "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
         "launches_per_step": per_step,
+        "kernels_per_layer": kernels_per_layer(cfg),
         "compute": ("Q.K on the scaled FP4 x FP8 MFMA (query split into fp8 hi + lo), P.V on fp16 MFMA "
                     "with the MXFP4 values dequantised to fp16, fp32 accumulate; window in bf16"),
         "roofline": {"kernel": "csa2_sparse_attn (attention + split-K combine)", "bound": "mfma",
@@ -346,6 +347,17 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, host_in, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def kernels_per_layer(cfg):
+    """Kernel launches of one layer's attention path, by layer mode (append not included).
+
+    csa2_index_topk launches the indexer and the top-K (two-level: coarse scores,
+    group top-K, fine scores, top-K); csa2_attend_layer always launches three
+    (sparse branch, window, combine).  Reuse layers run only the latter."""
+    index = 4 if cfg.top_groups else 2
+    modes = sorted(set(cfg.layers)) if cfg.name != "prefill" else ["F"]
+    return {m: (index + 3 if m in ("F", "R") else 3) for m in modes}
 
 
 def workload_config(cfg, rows):
