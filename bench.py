@@ -328,7 +328,7 @@ def main():
         "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
         "launches_per_step": per_step,
         "kernels_per_layer": kernels_per_layer(cfg),
-        "compute": ("Q.K on the scaled FP4 x FP8 MFMA (query split into fp8 hi + lo), P.V on fp16 MFMA "
+        "compute": ("Q.K on the scaled FP4 x FP6 MFMA (query split into three E2M3 terms), P.V on fp16 MFMA "
                     "with the MXFP4 values dequantised to fp16, fp32 accumulate; window in bf16"),
         "roofline": {"kernel": "csa2_sparse_attn (attention + split-K combine)", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",

@@ -110,8 +110,9 @@ int csa2_topk(const float* scores, int rows, int n, int k, int32_t* idx, int32_t
  * For each row r = (b, q) and head h: z_j = scale * (q_h . V_j) over the
  * present, visible entries j of the blocks idx[r][0..count[r]); V_j = the
  * dequantised entry; o = softmax(z) V (fp32), lse = log sum exp z.  An empty
- * selection gives o = 0, lse = -inf.  q . K runs on the scaled FP4 x FP8 MFMA
- * (the query split exactly into fp8 hi + lo parts, fp32 accumulation); the
+ * selection gives o = 0, lse = -inf.  q . K runs on the scaled FP4 x FP6 MFMA
+ * (each 32-dim block of the query split into three E2M3 terms that carry it to
+ * within 2^-11.7 of the block's largest value, fp32 accumulation); the
  * softmax weights are rounded to fp16 before the value product with V in fp16.
  *   q bf16 [B][Q][H][512]; cache as above; idx int32 [B][Q][top_k];
  *   count int32 [B][Q]; n_entries int32 [B]; q_pos int32 [B][Q] or NULL

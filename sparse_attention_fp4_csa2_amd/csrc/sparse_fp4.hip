@@ -15,8 +15,9 @@
 // overlaps the other's MFMAs.  A tile is 32 entries (4 blocks).  Per tile:
 //  * Q.K: lane (entry e = lane%32, half hh) loads 32 bytes of e's FP4 codes for
 //    the wave's dims and feeds them unconverted to v_mfma_scale_f32_32x32x64_
-//    f8f6f4 (A = E2M1 codes with their E8M0 scales, B = the query split into
-//    exact fp8 hi + lo parts): S^T[32 entries][32 heads] over 128 dims.
+//    f8f6f4 (A = E2M1 codes with their E8M0 scales, B = the query as three
+//    FP6 E2M3 terms with one E8M0 scale per 32 dims; an FP4 x FP6 product runs
+//    at twice the FP4 x FP8 rate): S^T[32 entries][32 heads] over 128 dims.
 //  * the 4 partial S^T tiles meet in LDS; wave dq sums the quarter of the tile
 //    it owns (entries 8dq..8dq+7), runs the online softmax on it and writes its
 //    quarter of P (fp16) back: every wave then reads the whole P^T tile as the
@@ -28,6 +29,9 @@
 //    tile that needs a move takes a rare uniform slow path.
 //  * workgroup order: the head groups of one (row, split) get linear ids 8
 //    apart, i.e. the same XCD, so their shared record reads meet in one L2.
+//  * of the two workgroups on a CU the older one wins instruction arbitration
+//    and finishes far ahead of the other; waves drop their priority on every
+//    other tile, which evens out the two.
 #include "device.h"
 #include "launch.h"
 
@@ -42,7 +46,6 @@ constexpr int MAX_SPLIT_BLOCKS = 2048;   // selected block ids one workgroup sta
 constexpr float LAZY_LOG2 = 8.0f;        // move the running max only when it grows by > 2^8
 constexpr float M_INIT = -1.0e30f;       // finite "no max yet": exp2(x - M_INIT) never NaN
 constexpr int VBIAS = 140;               // V' = V * 2^(VBIAS - vbase): code 6 at vbase -> 6*2^13
-constexpr int QLO_SHIFT = 4;             // fp8 lo part of a query carries 2^4 more resolution
 
 typedef int int32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
@@ -60,10 +63,11 @@ struct Lds {
   int32_t blk[MAX_SPLIT_BLOCKS];   // this split's selected block ids           8 KB
 };
 
-__device__ __forceinline__ floatx16 mfma_fp4_fp8(uint4 a, const int32x8& b, floatx16 c,
-                                                 uint32_t sa, uint32_t sb) {
+// A = 32 E2M1 codes, B = 32 E2M3 values (byte OPB of sb is B's scale)
+template <int OPB>
+__device__ __forceinline__ floatx16 mfma_fp4_fp6(uint4 a, const int32x8& b, floatx16 c, uint32_t sa, uint32_t sb) {
   const int32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, b, c, 4, 0, 0, (int)sa, 0, (int)sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, b, c, 4, 2, 0, (int)sa, OPB, (int)sb);
 }
 
 __device__ __forceinline__ floatx16 mfma_f16(uint4 a, uint4 b, floatx16 c) {
@@ -93,11 +97,16 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {    // v_cvt_pk_
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, halfx2));
 }
 
-// fp8 E4M3 (OCP) byte -> float, for the hi/lo query split
-__device__ __forceinline__ float fp8_byte_to_f32(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15, m = b & 7;
-  const float v = e ? ldexpf(1.f + (float)m * 0.125f, (int)e - 7) : ldexpf((float)m * 0.125f, -6);
-  return (b & 0x80) ? -v : v;
+typedef int int6v __attribute__((ext_vector_type(6)));
+typedef float floatx32 __attribute__((ext_vector_type(32)));
+
+// smallest e >= emin with mx * 2^-e <= 7.5 (the largest E2M3 value); 0 when mx
+// is 0 or not finite
+__device__ __forceinline__ int fp6_block_exp(float mx, int emin) {
+  if (!(mx > 0.f && mx < __builtin_inff())) return max(0, emin);
+  int e = ilogbf(mx) - 2;                      // mx * 2^-e in [4, 8)
+  if (ldexpf(mx, -e) > 7.5f) ++e;
+  return max(e, emin);
 }
 
 // (lane l, lane l^32) reductions: v_permlane32_swap gives {lane l%32, lane l%32 + 32}
@@ -165,76 +174,93 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   const uint32_t code_off = (e & 7) * 256 + 64 * dq + 16 * hh;
   const uint32_t sc_off = SCALE_OFF + (e & 7) * 16 + 4 * dq;
   const float c_log2 = p.scale_log2;
-
-  // ---- query: exact fp8 hi + lo B operands ------------------------------
-  // lane (head, hh), k-step s, byte i: dim 128dq + 64s + 32(i/16) + 16hh + i%16
-  int32x8 qhi[2], qlo[2];
-  uint32_t qsb_hi, qsb_lo;
-  {
-    const uint16_t* qrow = p.q + ((size_t)row * p.H + head) * D + 128 * dq + 16 * hh;
-    float qv[2][32];
-    float mx = 0.f;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const uint4* src = reinterpret_cast<const uint4*>(qrow + 64 * s + 32 * half);
-        const uint4 u0 = head_ok ? src[0] : make_uint4(0, 0, 0, 0);
-        const uint4 u1 = head_ok ? src[1] : make_uint4(0, 0, 0, 0);
-        const uint32_t wv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float a = __uint_as_float(wv[k] << 16);
-          const float c = __uint_as_float(wv[k] & 0xFFFF0000u);
-          qv[s][16 * half + 2 * k] = a;
-          qv[s][16 * half + 2 * k + 1] = c;
-          mx = fmaxf(mx, fmaxf(fabsf(a), fabsf(c)));
-        }
-      }
-    }
-    mx = pair_max(mx);
-    int cq = 0;
-    if (mx > 0.f && mx < __builtin_inff()) cq = 7 - ilogbf(mx);
-    const float f = ldexpf(1.f, cq), flo = ldexpf(1.f, QLO_SHIFT);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        int hw = 0, lw = 0;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float a0 = qv[s][4 * d + 2 * k] * f, a1 = qv[s][4 * d + 2 * k + 1] * f;
-          const int h2 = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-          const float h0 = fp8_byte_to_f32((uint32_t)h2 & 0xFF);
-          const float h1 = fp8_byte_to_f32(((uint32_t)h2 >> 8) & 0xFF);
-          const int l2 = __builtin_amdgcn_cvt_pk_fp8_f32((a0 - h0) * flo, (a1 - h1) * flo, 0, false);
-          hw |= (h2 & 0xFFFF) << (16 * k);
-          lw |= (l2 & 0xFFFF) << (16 * k);
-        }
-        qhi[s][d] = hw;
-        qlo[s][d] = lw;
-      }
-    }
-    qsb_hi = (uint32_t)(127 - cq);
-    qsb_lo = (uint32_t)(127 - cq - QLO_SHIFT);
-  }
-
-  {
-    const int i0 = 4 * t_begin, i1 = min(4 * t_end, n_items);
-    for (int i = i0 + tid; i < i1; i += 256) lds.blk[i - i0] = p.idx[(size_t)row * p.top_k + i];
-  }
-  __syncthreads();
-
-  // ---- tile helpers -----------------------------------------------------
-  auto fetch = [&](int t, Raw& r) {
+  auto read_id = [&](int t) -> int {
     const int item = 4 * t + (e >> 3);
-    const int blk = item < n_items_split ? lds.blk[min(item - 4 * t_begin, MAX_SPLIT_BLOCKS - 1)] : -1;
+    return item < n_items_split ? lds.blk[min(item - 4 * t_begin, MAX_SPLIT_BLOCKS - 1)] : -1;
+  };
+  auto fetch = [&](int blk, Raw& r) {
     r.valid = (uint32_t)blk < (uint32_t)nb_cap && blk * BLOCK + (e & 7) < lim;
     const uint32_t off = (uint32_t)blk * RECORD;
     r.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rec_rsrc, off + code_off, 0, 0));
     r.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rec_rsrc, off + code_off + 32, 0, 0));
     r.sc = __builtin_amdgcn_raw_buffer_load_b32(rec_rsrc, off + sc_off, 0, 0);
   };
+
+  // block ids of the first three tiles straight from memory, so that the first
+  // records are in flight while the query is converted; the whole split's ids
+  // are staged in LDS meanwhile
+  const int32_t* const idx_row = p.idx + (size_t)row * p.top_k;
+  auto mem_id = [&](int t) -> int {
+    const int item = 4 * t + (e >> 3);
+    const int v = idx_row[min(item, p.top_k - 1)];   // unconditional: the loads overlap
+    return item < n_items_split ? v : -1;
+  };
+  const int i_beg = 4 * t_begin;
+  const int stage0 = idx_row[min(i_beg + tid, p.top_k - 1)];
+  Raw r0, ra, rb;         // raw tiles, alternating: one is consumed, one is in flight
+  fetch(mem_id(t_begin), r0);
+  fetch(mem_id(t_begin + 1), ra);
+  int id_next = mem_id(t_begin + 2);   // this lane's block id for the next fetch (read a tile early)
+
+  // ---- query: three FP6 (E2M3) terms per 32-dim block -----------------
+  // lane (head, hh), k-step s: FP6 value k = dim 128dq + 64s + 32hh + k.  Each
+  // lane's 32 values are one block of the scaled MFMA with its own E8M0 scale:
+  // every term rounds (to nearest even) what the earlier terms left, at the
+  // scale of its own largest value.
+  int32x8 qt[3][2];       // [term][k-step]
+  uint32_t qsb = 0;       // scale bytes: [0] term 0 s0, [1] term 0 s1, [2] term 1 s0, [3] term 1 s1
+  uint32_t qsb2 = 0;      // [0] term 2 s0, [1] term 2 s1
+  {
+    const uint16_t* qrow = p.q + ((size_t)row * p.H + (head_ok ? head : 0)) * D + 128 * dq + 32 * hh;
+    const uint32_t m = head_ok ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float x[32];
+      const uint4* src = reinterpret_cast<const uint4*>(qrow + 64 * s);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint4 w = src[u];
+        const uint32_t wv[4] = {w.x & m, w.y & m, w.z & m, w.w & m};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[8 * u + 2 * k] = __uint_as_float(wv[k] << 16);
+          x[8 * u + 2 * k + 1] = __uint_as_float(wv[k] & 0xFFFF0000u);
+        }
+      }
+      // y0[i], y1[i] = values 2i, 2i + 1 of the block, relative to 2^etot
+      floatx16 y0, y1;
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) y0[i2] = x[2 * i2], y1[i2] = x[2 * i2 + 1];
+      int etot = 0;
+#pragma unroll
+      for (int term = 0; term < 3; ++term) {
+        float mx = 0.f;
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) mx = fmaxf(mx, fmaxf(fabsf(y0[i2]), fabsf(y1[i2])));
+        const int e = fp6_block_exp(mx, -127 - etot);
+        const float f = ldexpf(1.f, -e);
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) y0[i2] *= f, y1[i2] *= f;     // a power of two
+        etot += e;
+        const int6v c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(y0, y1, 1.f);
+        qt[term][s] = int32x8{c[0], c[1], c[2], c[3], c[4], c[5], 0, 0};
+        const uint32_t sbyte = (uint32_t)(127 + etot);
+        if (term < 2) qsb |= sbyte << (8 * (2 * term + s));
+        else qsb2 |= sbyte << (8 * s);
+        if (term < 2) {
+          const floatx32 d = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, 1.f);
+#pragma unroll
+          for (int i2 = 0; i2 < 16; ++i2) y0[i2] -= d[2 * i2], y1[i2] -= d[2 * i2 + 1];   // exact
+        }
+      }
+    }
+  }
+
+  if (i_beg + tid < n_items_split) lds.blk[tid] = stage0;
+  for (int i = i_beg + tid + 256; i < n_items_split; i += 256) lds.blk[i - i_beg] = idx_row[i];
+  __syncthreads();
+
+  // ---- tile helpers -----------------------------------------------------
   // largest scale byte of the wave's groups in the tile (every fetched entry,
   // so no dequantised value can overflow fp16), folded into the running base
   auto raise_base = [&](const Raw& r, int cur) -> int {
@@ -267,10 +293,12 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
     const uint32_t s8 = r.sc >> (8 * hh);
     const uint32_t s8b = s8 >> 16;
     floatx16 sacc = floatx16{};
-    sacc = mfma_fp4_fp8(r.c0, qhi[0], sacc, s8, qsb_hi);
-    sacc = mfma_fp4_fp8(r.c0, qlo[0], sacc, s8, qsb_lo);
-    sacc = mfma_fp4_fp8(r.c1, qhi[1], sacc, s8b, qsb_hi);
-    sacc = mfma_fp4_fp8(r.c1, qlo[1], sacc, s8b, qsb_lo);
+    sacc = mfma_fp4_fp6<0>(r.c0, qt[0][0], sacc, s8, qsb);
+    sacc = mfma_fp4_fp6<2>(r.c0, qt[1][0], sacc, s8, qsb);
+    sacc = mfma_fp4_fp6<0>(r.c0, qt[2][0], sacc, s8, qsb2);
+    sacc = mfma_fp4_fp6<1>(r.c1, qt[0][1], sacc, s8b, qsb);
+    sacc = mfma_fp4_fp6<3>(r.c1, qt[1][1], sacc, s8b, qsb);
+    sacc = mfma_fp4_fp6<1>(r.c1, qt[2][1], sacc, s8b, qsb2);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       lds.sp[sbuf][dq][j][lane] = floatx4{sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3]};
@@ -293,12 +321,8 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   // 16-entry k-step in order (k = 8hh' + j is entry 16ks2 + 8hh' + j)
   const int pslot = 8 * dq + 4 * hh;
 
-  Raw ra, rb;             // raw tiles, alternating: one is consumed, one is in flight
   uint32_t vmask_cur = 0;
   if (t_begin < t_end) {
-    Raw r0;
-    fetch(t_begin, r0);
-    fetch(t_begin + 1, ra);
     base_v = raise_base(r0, 0);
     base_o = base_v;
     write_vc(t_begin & 1, r0, base_v);
@@ -384,8 +408,11 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   // S, P, flags and the V tile are double-buffered by tile parity.
   auto tile_step = [&](int t, Raw& rc, Raw& rl) {
     const int buf = t & 1;
+    if (t & 1) __builtin_amdgcn_s_setprio(1);    // wave priority alternates by tile
+    else __builtin_amdgcn_s_setprio(0);
     const bool more = t + 1 < t_end;
-    fetch(t + 2, rl);
+    fetch(id_next, rl);
+    id_next = read_id(t + 3);
     floatx4 sw[4];
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) sw[w2] = lds.sp[buf][w2][dq][lane];
