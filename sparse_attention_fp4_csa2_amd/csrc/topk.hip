@@ -13,8 +13,12 @@
 // over the range the row's scores actually occupy (a fixed top-11-bit digit
 // puts a typical row into a handful of bins, and the LDS atomics on those few
 // bins serialise).  Each pass fixes up to 11 more bits of the K-th largest
-// key; then a block-wide scan compacts the ids with key > tau, plus the
-// lowest-id ties at tau, in id order.
+// key; once the bin holding it has at most 64 keys, those keys go to LDS and
+// one wave ranks them directly instead of running further passes.  A larger
+// bin's own key range places the next pass's digits (skipping the bits all its
+// keys share), and a bin of equal keys ends the search (planted blocks of equal
+// score pile up there).  Then a block-wide scan compacts the ids with key >
+// tau, plus the lowest-id ties at tau, in id order.
 #include "device.h"
 #include "launch.h"
 
@@ -23,6 +27,7 @@ namespace csa2 {
 namespace {
 
 constexpr int HIST_BINS = 2048;
+constexpr uint32_t RANK_MAX = 64;   // a boundary bin this small is ranked directly
 
 // Wave-wide inclusive prefix sum: four DPP row shifts (1, 2, 4, 8) within each
 // 16-lane row, then row broadcasts of lane 15 and lane 31.
@@ -60,7 +65,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sbuf, 
 
 // RANGE: digits relative to the row's key range (min/max reduction first);
 // otherwise fixed digits from bit 31 (11 + 11 + 10 bits), which skips the
-// reduction and pays off when the scores spread over many bins anyway.
+// reduction (short rows).
 template <int TPB, int C, bool RANGE>
 __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ scores, int n, int k, int vec,
                                                    const int32_t* __restrict__ gsel, int n_gsel,
@@ -71,10 +76,12 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ sco
   __shared__ uint32_t hist[HIST_BINS];
   __shared__ uint32_t sbuf[NW];
   __shared__ uint32_t sred[NW][3];
-  __shared__ uint32_t sh_digit, sh_above;
+  __shared__ uint32_t sh_digit, sh_above, sh_cnt;
+  __shared__ uint32_t rk_key[RANK_MAX], rk_n, sh_tau, sh_need;
   const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const float* s = scores + (size_t)row * n;
   const int i0 = t * C;
+  if (t == 0) rk_n = 0;
 
   uint32_t key[C];
 #pragma unroll
@@ -90,6 +97,7 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ sco
   }
 
   bool all = false;               // every candidate is kept (block-uniform)
+  bool ranked = false;            // tau and its tie count are in sh_tau, sh_need
   uint32_t prefix = 0, kleft = (uint32_t)k;
   int pos = 32;
   if constexpr (RANGE) {
@@ -157,18 +165,75 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ sco
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
       const int r = BPT * t + j;
-      if (r < nb && before < kleft && kleft <= before + h[j]) sh_digit = nb - 1 - r, sh_above = before;
+      if (r < nb && before < kleft && kleft <= before + h[j])
+        sh_digit = nb - 1 - r, sh_above = before, sh_cnt = h[j];
       before += h[j];
     }
     __syncthreads();
     prefix |= sh_digit << sh;
     kleft -= sh_above;
     pos = sh;
+    if (pos > 0 && sh_cnt <= RANK_MAX) {
+      // rank step: the keys of the boundary bin go to LDS; lane j of wave 0
+      // counts the keys above and at its own key, and the lane whose key is the
+      // kleft-th largest of the bin publishes it (tau) and how many of its
+      // equal keys are kept
+      const uint32_t m2 = ~0u << pos;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const uint32_t x = key[c];
+        if (x && (x & m2) == prefix) rk_key[atomicAdd(&rk_n, 1u)] = x;
+      }
+      __syncthreads();
+      if (wv == 0) {
+        const uint32_t cnt = rk_n;
+        const uint32_t kj = (uint32_t)lane < cnt ? rk_key[lane] : 0u;
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t i = 0; i < cnt; ++i) {
+          const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)kj, (int)i);
+          gt += ki > kj;
+          ge += ki >= kj;
+        }
+        if ((uint32_t)lane < cnt && gt < kleft && kleft <= ge) sh_tau = kj, sh_need = kleft - gt;
+      }
+      __syncthreads();
+      ranked = true;
+      break;
+    }
+    if (pos > 0) {
+      // a large boundary bin: its key range places the next digits (the bits
+      // its keys share are skipped), or, when all its keys are equal, is tau
+      const uint32_t m2 = ~0u << pos;
+      uint32_t bmin = 0xffffffffu, bmax = 0u;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const uint32_t x = key[c];
+        if (x && (x & m2) == prefix) bmin = min(bmin, x), bmax = max(bmax, x);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        bmin = min(bmin, (uint32_t)__shfl_xor((int)bmin, o, 64));
+        bmax = max(bmax, (uint32_t)__shfl_xor((int)bmax, o, 64));
+      }
+      if (lane == 0) sred[wv][0] = bmin, sred[wv][1] = bmax;
+      __syncthreads();
+      bmin = 0xffffffffu, bmax = 0u;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) bmin = min(bmin, sred[w][0]), bmax = max(bmax, sred[w][1]);
+      if (bmin == bmax) {
+        if (t == 0) sh_tau = bmin, sh_need = kleft;
+        __syncthreads();
+        ranked = true;
+        break;
+      }
+      pos = 32 - __clz(bmin ^ bmax);
+      prefix = pos >= 32 ? 0u : (bmin & (~0u << pos));
+    }
   }
   // keep x > tau, plus the first need_eq candidates (in id order) with x == tau;
   // tau >= 1 unless every candidate is kept, when tau = 0 keeps all x >= 1
-  const uint32_t tau = all ? 0u : prefix;
-  const uint32_t need_eq = all ? 0u : kleft;
+  const uint32_t tau = all ? 0u : ranked ? sh_tau : prefix;
+  const uint32_t need_eq = all ? 0u : ranked ? sh_need : kleft;
 
   uint32_t gt = 0, eq = 0;
 #pragma unroll
@@ -200,19 +265,19 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ sco
   if (t == 0) count[row] = (int32_t)total;
 }
 
-// n <= 65536.  Rows of up to 8192 scores run on 256 threads with fixed
-// digits; longer rows use 1024 threads and range-relative digits when there
-// are too few rows to fill the chip (there one row's latency is the cost, and
-// candidates drawn from a few top groups crowd into few fixed-digit bins).
+// n <= 65536.  Rows of up to 1024 scores run on 256 threads with fixed digits
+// (one short pass); longer ones use range-relative digits, on 256 threads, or
+// on 1024 when the row is long and there are too few rows to fill the chip
+// (there one row's latency is the cost).
 int launch_topk(const float* scores, int rows, int n, int k, const int32_t* gsel, int n_gsel,
                 int32_t* idx, int32_t* count, hipStream_t stream) {
   const int vec = (n % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
 #define CSA2_TOPK(T, C, R) \
   topk_kernel<T, C, R><<<rows, T, 0, stream>>>(scores, n, k, vec, gsel, n_gsel, idx, count)
   if (n <= 256 * 4) CSA2_TOPK(256, 4, false);
-  else if (n <= 256 * 16) CSA2_TOPK(256, 16, false);
-  else if (n <= 256 * 32) CSA2_TOPK(256, 32, false);
-  else if (n <= 256 * 64 && rows >= 128) CSA2_TOPK(256, 64, false);
+  else if (n <= 256 * 16) CSA2_TOPK(256, 16, true);
+  else if (n <= 256 * 32) CSA2_TOPK(256, 32, true);
+  else if (n <= 256 * 64 && rows >= 128) CSA2_TOPK(256, 64, true);
   else if (n <= 1024 * 16) CSA2_TOPK(1024, 16, true);
   else CSA2_TOPK(1024, 64, true);
 #undef CSA2_TOPK

@@ -32,7 +32,7 @@ def gpu_topk(scores, k):
                                  (1000, 1), (65536, 2048)])
 def test_topk_from_scores_bit_exact_with_ties(n, k):
     rng = rng_for(n * 7 + k)
-    rows = 7
+    rows = 10
     s = np.empty((rows, n), dtype=np.float32)
     s[0] = rng.standard_normal(n)
     s[1] = rng.integers(-3, 4, size=n)                 # heavy ties, negatives, zeros
@@ -45,6 +45,17 @@ def test_topk_from_scores_bit_exact_with_ties(n, k):
     s[5, ::5] = np.nan                                  # NaN = non-candidate
     s[6] = rng.choice(np.array([0.0, -0.0], np.float32), n)   # +0 and -0 tie; rank k among them
     s[6, rng.choice(n, max(1, min(n, k) // 2), replace=False)] = 1.0
+    # a few equal keys straddling rank k amid distinct ones: the bin holding
+    # the k-th key is small, so the kernel ranks it directly
+    s[7] = rng.standard_normal(n)
+    order = np.argsort(-s[7].astype(np.float64), kind="stable")
+    lo, hi = max(0, min(n, k) - 4), min(n, k + 3)
+    s[7, order[lo:hi]] = s[7, order[lo]]
+    # planted-like rows: one score shared by exactly k blocks (then by k + 5),
+    # far above the rest, beside a few negatives: the boundary bin is one value
+    for r, extra in ((8, 0), (9, 5)):
+        s[r] = rng.standard_normal(n) * 20.0
+        s[r, rng.choice(n, min(n, k + extra), replace=False)] = 317.9581
     got, cnt = gpu_topk(s, k)
     for r in range(rows):
         ref_in = np.where(np.isnan(s[r]), -np.inf, s[r]).astype(np.float64)
