@@ -347,14 +347,11 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
   p.scale_log2 = scale * 1.4426950408889634f;
   p.splits = s_sparse;
   set_partials(p, ws, l, total, 0);
-  int rc = launch_sparse_fp4(p, st);
-  if (!rc) {
-    AttnParams pw = p;
-    pw.cache = nullptr; pw.idx = nullptr; pw.count = nullptr; pw.n_entries = nullptr;
-    pw.swa = swa_kv; pw.swa_len = swa_len; pw.swa_pos0 = swa_pos0; pw.W = W; pw.Lw = Lw;
-    pw.splits = s_window; pw.split_base = s_sparse;
-    rc = launch_window(pw, st);
-  }
+  AttnParams pw = p;
+  pw.cache = nullptr; pw.idx = nullptr; pw.count = nullptr; pw.n_entries = nullptr;
+  pw.swa = swa_kv; pw.swa_len = swa_len; pw.swa_pos0 = swa_pos0; pw.W = W; pw.Lw = Lw;
+  pw.splits = s_window; pw.split_base = s_sparse;
+  int rc = launch_attend(p, pw, st);   // both branches in one launch
   if (!rc) rc = combine_partials(ws, l, rows, total, H, nullptr, nullptr, out, lse_out, st);
   return launch_status(rc);
 }

@@ -56,12 +56,15 @@ struct AttnParams {
   int split_base;           // this launch writes splits [split_base, split_base + splits)
 };
 
-// bf16 window (attention.hip): 64-head workgroups, few tiles per row
+// bf16 window (attention.hip): 32-head workgroups, few tiles per row
 int window_splits(int rows, int H, int n_tiles);
 int launch_window(const AttnParams& p, hipStream_t stream);
 // MXFP4 selected blocks (sparse_fp4.hip): 32-head workgroups, two per CU
 int sparse_fp4_splits(int rows, int H, int n_tiles);
 int launch_sparse_fp4(const AttnParams& p, hipStream_t stream);
+// Both branches of a layer in one launch (sparse_fp4.hip): the sparse
+// workgroups, then the window's; each writes its own partial splits.
+int launch_attend(const AttnParams& ps, const AttnParams& pw, hipStream_t stream);
 
 // Merge split partials (fp16 o, exponent, lse; and an optional fp32 extra
 // branch) -> out [rows][H][512], lse [rows][H].

@@ -34,6 +34,7 @@
 //    other tile, which evens out the two.
 #include "device.h"
 #include "launch.h"
+#include "window_body.h"
 
 namespace csa2 {
 
@@ -135,10 +136,9 @@ constexpr int BUF_DWORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_units, int hgroups) {
-  __shared__ Lds lds;
+// One workgroup's share; L = its index within the sparse grid
+__device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, int hgroups, int L, Lds& lds) {
   // ---- workgroup -> (row, split, head group), XCD-aware ------------------
-  const int L = blockIdx.x;
   const int unit = (L / (8 * hgroups)) * 8 + (L & 7);
   const int hgi = (L >> 3) % hgroups;
   if (unit >= n_units) return;
@@ -497,6 +497,25 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   }
 }
 
+__global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_units, int hgroups) {
+  __shared__ Lds lds;
+  sparse_body(p, n_units, hgroups, blockIdx.x, lds);
+}
+
+// Both branches of one layer in one launch: the sparse workgroups come first,
+// the window's after them, so the window runs in the slots the sparse
+// workgroups free as they finish (the first of each CU's pair finishes well
+// ahead of the second) instead of after the last of them.
+__global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_units, int hgroups,
+                                                        int n_sparse_wg, AttnParams pw, int whgroups) {
+  __shared__ union {
+    Lds s;
+    win::WinLds w;
+  } lds;
+  if ((int)blockIdx.x < n_sparse_wg) sparse_body(ps, n_units, hgroups, blockIdx.x, lds.s);
+  else win::window_body(pw, whgroups, (int)blockIdx.x - n_sparse_wg, lds.w);
+}
+
 int sparse_fp4_splits(int rows, int H, int n_tiles) {
   const int hgroups = (H + 31) / 32;
   const int wgs = rows * hgroups;
@@ -517,6 +536,18 @@ int launch_sparse_fp4(const AttnParams& p, hipStream_t stream) {
   const long long n_wg = (long long)groups * 8 * hgroups;
   if (n_wg > 0x7FFFFFFF) return -4;
   sparse_fp4_kernel<<<dim3((unsigned)n_wg), 256, 0, stream>>>(p, n_units, hgroups);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_attend(const AttnParams& ps, const AttnParams& pw, hipStream_t stream) {
+  const int hgroups = (ps.H + 31) / 32;
+  const int n_units = ps.rows * ps.splits;
+  const long long n_sparse = (long long)((n_units + 7) / 8) * 8 * hgroups;   // a multiple of 8
+  const int whgroups = (pw.H + 31) / 32;
+  const long long n_window = (long long)((pw.rows * pw.splits + 7) / 8) * 8 * whgroups;
+  if (n_sparse + n_window > 0x7FFFFFFF) return -4;
+  attend_kernel<<<dim3((unsigned)(n_sparse + n_window)), 256, 0, stream>>>(ps, n_units, hgroups, (int)n_sparse,
+                                                                           pw, whgroups);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
