@@ -353,11 +353,12 @@ def kernels_per_layer(cfg):
     """Kernel launches of one layer's attention path, by layer mode (append not included).
 
     csa2_index_topk launches the indexer and the top-K (two-level: coarse scores,
-    group top-K, fine scores, top-K); csa2_attend_layer always launches three
-    (sparse branch, window, combine).  Reuse layers run only the latter."""
+    group top-K, fine scores, top-K); csa2_attend_layer always launches two
+    (both branches in one kernel, then the combine).  Reuse layers run only
+    the latter."""
     index = 4 if cfg.top_groups else 2
     modes = sorted(set(cfg.layers)) if cfg.name != "prefill" else ["F"]
-    return {m: (index + 3 if m in ("F", "R") else 3) for m in modes}
+    return {m: (index + 2 if m in ("F", "R") else 2) for m in modes}
 
 
 def workload_config(cfg, rows):
