@@ -27,8 +27,9 @@
 //    (entry-major) and come back transposed with ds_read_b64_tr_b16.
 //  * the running max moves lazily (only when a head's max grows by > 2^8); a
 //    tile that needs a move takes a rare uniform slow path.
-//  * workgroup order: the head groups of one (row, split) get linear ids 8
-//    apart, i.e. the same XCD, so their shared record reads meet in one L2.
+//  * workgroup order: each XCD takes a contiguous range of (row, split, head
+//    group), so a row's query and (between its two head groups) its records
+//    are read from HBM once and then hit that XCD's L2.
 //  * of the two workgroups on a CU the older one wins instruction arbitration
 //    and finishes far ahead of the other; waves drop their priority on every
 //    other tile, which evens out the two.
@@ -139,8 +140,14 @@ constexpr int BUF_DWORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
 // One workgroup's share; L = its index within the sparse grid
 __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, int hgroups, int L, Lds& lds) {
   // ---- workgroup -> (row, split, head group), XCD-aware ------------------
-  const int unit = (L / (8 * hgroups)) * 8 + (L & 7);
-  const int hgi = (L >> 3) % hgroups;
+  // XCD x (= L % 8) runs the x-th contiguous eighth of the (row, split, head
+  // group) order, so a row's splits and head groups share one XCD's L2: the
+  // row's query comes from HBM once, and the two head groups of a split (ids
+  // 8 apart, dispatched together) share their record reads
+  const int per_xcd = ((n_units + 7) / 8) * hgroups;
+  const int u = (L & 7) * per_xcd + (L >> 3);
+  const int unit = u / hgroups;
+  const int hgi = u - unit * hgroups;
   if (unit >= n_units) return;
   const int row = unit / p.splits;
   const int split = unit - row * p.splits;
