@@ -140,14 +140,23 @@ constexpr int BUF_DWORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
 // One workgroup's share; L = its index within the sparse grid
 __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, int hgroups, int L, Lds& lds) {
   // ---- workgroup -> (row, split, head group), XCD-aware ------------------
-  // XCD x (= L % 8) runs the x-th contiguous eighth of the (row, split, head
-  // group) order, so a row's splits and head groups share one XCD's L2: the
-  // row's query comes from HBM once, and the two head groups of a split (ids
-  // 8 apart, dispatched together) share their record reads
-  const int per_xcd = ((n_units + 7) / 8) * hgroups;
-  const int u = (L & 7) * per_xcd + (L >> 3);
-  const int unit = u / hgroups;
-  const int hgi = u - unit * hgroups;
+  // With several splits, XCD x (= L % 8) runs the x-th contiguous eighth of
+  // the (row, split, head group) order, so a row's splits and head groups
+  // share one XCD's L2: the row's query comes from HBM once, and the two head
+  // groups of a split (ids 8 apart, dispatched together) share their record
+  // reads.  With one split (many rows per sequence, as in prefill) unit u goes
+  // to XCD u % 8 and its head groups to ids 8 apart: measured to fetch a
+  // quarter of the L2 misses of the contiguous order there.
+  int unit, hgi;
+  if (p.splits > 1) {
+    const int per_xcd = ((n_units + 7) / 8) * hgroups;
+    const int u = (L & 7) * per_xcd + (L >> 3);
+    unit = u / hgroups;
+    hgi = u - unit * hgroups;
+  } else {
+    unit = (L / (8 * hgroups)) * 8 + (L & 7);
+    hgi = (L >> 3) % hgroups;
+  }
   if (unit >= n_units) return;
   const int row = unit / p.splits;
   const int split = unit - row * p.splits;
