@@ -61,6 +61,10 @@ def parse(argv=None):
                     choices=["tiny", "decode64k", "decode1m", "layers128k", "prefill", "specdec64k"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="reps of the cold timings (a 1 GiB write before each evicts L2 and the 256 MB "
+                         "last-level cache); 0 skips them")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak reference runs")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain fp32 copy kernel over this many bytes "
                          "(the calibration point for rocprofv3 FETCH_SIZE / WRITE_SIZE runs)")
@@ -299,6 +303,28 @@ def main():
     attn_tflops = flops_attn / (t_attn * 1e-3) / 1e12
     kv_tbps = n_ent * 272 / (t_attn * 1e-3) / 1e12
 
+    # cold: every timed call starts with L2 and the last-level cache holding a
+    # 1 GiB scratch write instead of the workload's data (median of the reps)
+    cold = None
+    if args.cold_reps > 0:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+        def cold_ms(fn):
+            ts = []
+            for i in range(args.cold_reps):
+                scratch.fill_(float(i))
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            return float(np.median(ts))
+
+        cold = {"step": round(cold_ms(wl.step), 4), "sparse_attn": round(cold_ms(wl.sparse_attn_call), 4)}
+        del scratch
+    peaks = None if args.no_peaks else measured_peaks(torch, stream)
+
     if args.copy_bytes > 0:
         n = args.copy_bytes // 4
         src = torch.randn(n, device="cuda")
@@ -337,6 +363,12 @@ def main():
                      "flops_per_launch": flops_attn},
         "setup_s": round(gen_s, 1),
     }
+    if cold is not None:
+        result["cold_ms"] = cold
+        result["cold_value"] = round(rows / (cold["step"] * 1e-3), 1)
+    if peaks is not None:
+        result["measured_peaks"] = peaks
+        result["roofline"]["frac_of_measured_gemm"] = round(attn_tflops / peaks["bf16_gemm_TFLOPs"], 4)
     if not prefill:
         idx_bytes = wl.B * cfg.N * 128 if not cfg.top_groups else \
             wl.B * (cfg.cap // 512 * 256 + cfg.top_groups * 512 * 128)
@@ -347,6 +379,36 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, host_in, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def measured_peaks(torch, stream):
+    """Reference rates measured in the same session: a 1 GiB fp32 copy (read +
+    write bytes over time) and a dense 8192^3 bf16 GEMM through torch.matmul
+    (the vendor GEMM library); medians of 10 runs each."""
+    def med(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = med(lambda: dst.copy_(src))
+    del src, dst
+    n = 8192
+    a = torch.ones((n, n), dtype=torch.bfloat16, device="cuda")
+    b = torch.ones((n, n), dtype=torch.bfloat16, device="cuda")
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    t_mm = med(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    return {"copy_GBps": round(2 * (1 << 30) / (t_copy * 1e-3) / 1e9, 1),
+            "bf16_gemm_TFLOPs": round(2.0 * n ** 3 / (t_mm * 1e-3) / 1e12, 1)}
 
 
 def kernels_per_layer(cfg):
