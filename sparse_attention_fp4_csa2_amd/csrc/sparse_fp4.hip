@@ -11,7 +11,7 @@
 //
 // Organisation: one workgroup = (row, split, group of 32 heads), 4 waves; wave
 // dq owns latent dims [128dq, 128dq + 128) for all 32 heads.  Two workgroups
-// fit on a CU (<= 256 registers per lane, ~71 KB LDS), so one wave's VALU work
+// fit on a CU (<= 256 registers per lane, ~48 KB LDS), so one wave's VALU work
 // overlaps the other's MFMAs.  A tile is 32 entries (4 blocks).  Per tile:
 //  * Q.K: lane (entry e = lane%32, half hh) loads 32 bytes of e's FP4 codes for
 //    the wave's dims and feeds them unconverted to v_mfma_scale_f32_32x32x64_
@@ -22,9 +22,13 @@
 //    it owns (entries 8dq..8dq+7), runs the online softmax on it and writes its
 //    quarter of P (fp16) back: every wave then reads the whole P^T tile as the
 //    B operand of O^T += V^T P^T (v_mfma_f32_32x32x16_f16).
-//  * V: the same codes, dequantised with v_cvt_scalef32_pk_f16_fp4 to fp16
-//    relative to a per-wave power-of-two base, go to the wave's own LDS tile
-//    (entry-major) and come back transposed with ds_read_b64_tr_b16.
+//  * V never touches LDS: the same codes, still in registers one tile later,
+//    are the A operand of a scaled FP4 x FP4 MFMA against the identity, which
+//    applies each entry's E8M0 scale (and a per-wave power-of-two base through
+//    the B scale) and leaves V' fp32 with entries along the accumulator rows,
+//    i.e. already transposed for the P.V A operand; v_cvt_pk_f16_f32 packs it.
+//    Per 32 x 32 block that is one fast-rate MFMA and 8 conversions instead of
+//    16 VALU dequantisation steps plus an LDS round trip.
 //  * the running max moves lazily (only when a head's max grows by > 2^8); a
 //    tile that needs a move takes a rare uniform slow path.
 //  * workgroup order: each XCD takes a contiguous range of (row, split, head
@@ -42,7 +46,6 @@ namespace csa2 {
 namespace {
 
 constexpr int TILE = 32;                 // entries per tile
-constexpr int VCROWU = 5;                // 16-byte units per V code row: 4 data + 1 pad
 constexpr int PROW = 40;                 // fp16 slots per P row (32 entries + 8 pad)
 constexpr int MAX_SPLIT_BLOCKS = 2048;   // selected block ids one workgroup stages in LDS
 constexpr float LAZY_LOG2 = 8.0f;        // move the running max only when it grows by > 2^8
@@ -51,12 +54,9 @@ constexpr int VBIAS = 140;               // V' = V * 2^(VBIAS - vbase): code 6 a
 
 typedef int int32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 struct Lds {
   floatx4 sp[2][4][4][64];         // [buffer][wave][quarter][lane] partial S^T  32 KB
-  uint4 vc[2][4][TILE * VCROWU];   // [buffer][wave][entry * VCROWU + unit] V    20 KB
-  uint16_t vf[2][4][4][32];        // [buffer][wave][group][entry] fp16 factors   2 KB
   uint16_t pb[2][32 * PROW];       // [buffer][head * PROW + slot] fp16 P        5 KB
   float qmax[2][4][32];            // [buffer][wave][head] quarter max of z*log2e
   int flag[2][4];                  // [buffer][wave] quarter needs a max move
@@ -64,6 +64,13 @@ struct Lds {
   int emax[4][32];                 // epilogue: per-wave exponent of the largest |o|
   int32_t blk[MAX_SPLIT_BLOCKS];   // this split's selected block ids           8 KB
 };
+
+// A = 32 E2M1 codes, B = 32 E2M1 codes (byte 0 of each scale operand)
+__device__ __forceinline__ floatx16 mfma_fp4_fp4(uint4 a, uint4 b, uint32_t sa, uint32_t sb) {
+  const int32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const int32x8 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, floatx16{}, 4, 4, 0, (int)sa, 0, (int)sb);
+}
 
 // A = 32 E2M1 codes, B = 32 E2M3 values (byte OPB of sb is B's scale)
 template <int OPB>
@@ -79,22 +86,7 @@ __device__ __forceinline__ floatx16 mfma_f16(uint4 a, uint4 b, floatx16 c) {
 
 typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) v2i lds_v2i;
 
-// 8 E2M1 codes (nibble j = element j) -> fp16, times the fp16 factors f[j]
-__device__ __forceinline__ uint4 codes_to_f16(int codes, halfx8 f) {
-  const halfx2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)codes, 1.f, 0);
-  const halfx2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)codes, 1.f, 1);
-  const halfx2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)codes, 1.f, 2);
-  const halfx2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)codes, 1.f, 3);
-  uint4 r;
-  r.x = __builtin_bit_cast(uint32_t, v0 * halfx2{f[0], f[1]});
-  r.y = __builtin_bit_cast(uint32_t, v1 * halfx2{f[2], f[3]});
-  r.z = __builtin_bit_cast(uint32_t, v2 * halfx2{f[4], f[5]});
-  r.w = __builtin_bit_cast(uint32_t, v3 * halfx2{f[6], f[7]});
-  return r;
-}
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {    // v_cvt_pk_f16_f32, RNE
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, halfx2));
 }
@@ -213,7 +205,7 @@ __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, in
   };
   const int i_beg = 4 * t_begin;
   const int stage0 = idx_row[min(i_beg + tid, p.top_k - 1)];
-  Raw r0, ra, rb;         // raw tiles, alternating: one is consumed, one is in flight
+  Raw r0, ra, rb, rx;     // raw tiles (see the tile loop)
   fetch(mem_id(t_begin), r0);
   fetch(mem_id(t_begin + 1), ra);
   int id_next = mem_id(t_begin + 2);   // this lane's block id for the next fetch (read a tile early)
@@ -286,23 +278,6 @@ __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, in
     if (__any(smax > cur)) return max(cur, wave_max_int(smax));
     return cur;
   };
-  // V goes through the wave's LDS tile as FP4 codes (a quarter of the fp16
-  // bytes) plus one fp16 factor 2^(sb - vb + VBIAS - 127) per (entry, 32-dim
-  // group); ds_read_b64_tr_b4 transposes the codes (result lane i, nibble n =
-  // nibble i%16 of the word of lane n of its 16-lane group), and the lane
-  // rescales its 16 values per entry after the E2M1 -> fp16 conversion.
-  auto write_vc = [&](int vbuf, const Raw& r, int vb) {
-    uint4* const vcrow = &lds.vc[vbuf][dq][e * VCROWU];
-    vcrow[hh] = r.c0;                 // dims 32hh + [0, 32) of the wave's 128
-    vcrow[2 + hh] = r.c1;             // dims 64 + 32hh + [0, 32)
-#pragma unroll
-    for (int g2 = 0; g2 < 2; ++g2) {  // lane hh writes the factors of groups 2hh, 2hh + 1
-      const int g = 2 * hh + g2;
-      const int x = (int)((r.sc >> (8 * g)) & 0xFF) - vb + VBIAS - 127;   // <= 13
-      const _Float16 f = (_Float16)ldexpf(1.f, x);
-      lds.vf[vbuf][dq][g][e] = __builtin_bit_cast(uint16_t, f);
-    }
-  };
   // Q.K partial S^T over the wave's 128 dims -> LDS
   auto qk_s = [&](int sbuf, const Raw& r) {
     // the MFMA reads the E8M0 scale from byte 0 of its scale operand
@@ -327,58 +302,59 @@ __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, in
   float l_lane = 0.f;     // softmax denominator over this lane's quarter entries
   int base_o = 0;         // O^T is in units of 2^(base_o - VBIAS)
   int base_v = 0;         // base of the newest dequantised V tile
-  uint4 va[2][4];         // V^T A fragments (fp16) of the previous tile, [ks2][mt]
   floatx4 sq_prev = floatx4{};   // the previous tile's logits quarter (for a late max move)
   float pr_prev[4] = {0.f, 0.f, 0.f, 0.f};   // ... and its softmax weights
   uint4 pfr[2];           // P^T B fragments of the previous tile, [ks2]
   int base_prev = 0;      // base of those V^T fragments
 
-  // P slot of entry 8dq + 4hh + r: the V^T fragments hold the entries of a
-  // 16-entry k-step in order (k = 8hh' + j is entry 16ks2 + 8hh' + j)
-  const int pslot = 8 * dq + 4 * hh;
+  // V^T fragments come out of the dequantising MFMA with k = 8hh' + j of k-step
+  // ks2 holding entry 16ks2 + 8(j/4) + 4hh' + j%4 (its output row order); P^T
+  // uses the same order, so entry 8dq + 4hh + r sits at P slot pslot + r
+  const int pslot = 16 * (dq >> 1) + 8 * hh + 4 * (dq & 1);
+  // identity B operands of that MFMA (E2M1 1.0 = code 2): bid[h'] selects the
+  // 32 dims 32h' + [0, 32) of a 64-dim k-step (lane (n, hb) holds k = 32hb + [0, 32))
+  uint4 bid[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const uint32_t v = hh == h2 ? 2u << (4 * (e & 7)) : 0u;
+    const int d = e >> 3;
+    bid[h2] = make_uint4(d == 0 ? v : 0u, d == 1 ? v : 0u, d == 2 ? v : 0u, d == 3 ? v : 0u);
+  }
 
   uint32_t vmask_cur = 0;
   if (t_begin < t_end) {
-    base_v = raise_base(r0, 0);
+    base_v = raise_base(r0, 13);     // >= 13: the dequantising MFMA's B scale byte 267 - base fits
     base_o = base_v;
-    write_vc(t_begin & 1, r0, base_v);
     qk_s(t_begin & 1, r0);
     vmask_cur = (uint32_t)__ballot(r0.valid);
   }
   __syncthreads();
 
-  auto issue_pv = [&]() {
+  // P(t-1).V(t-1): V^T of each 32-dim group straight from the tile's codes in
+  // registers: a scaled FP4 x FP4 MFMA against the identity applies each
+  // entry's E8M0 scale (A scale) and 2^(VBIAS - base) (B scale), giving fp32
+  // V'[entry][dim] in the accumulator layout, whose rows are the A operand's k
+  auto issue_pv = [&](const Raw& r) {
     if (base_prev != base_o) {        // that tile's V used a higher base: rescale O exactly
       const float f = ldexpf(1.f, base_o - base_prev);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) oacc[mt] *= f;
       base_o = base_prev;
     }
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        oacc[mt] = mfma_f16(va[ks2][mt], pfr[ks2], oacc[mt]);
-      }
-  };
-
-  // transposed code reads: source lane n of each 16-lane group points at entry
-  // 16(n/8) + 8(lane/32) + n%8, the 16 dims 32mt + 16((lane/16) & 1) + [0, 16)
-  const int tr_n = lane & 15;
-  const int tr_entry = 16 * (tr_n >> 3) + 8 * hh + (tr_n & 7);
-  auto read_vt = [&](int vbuf) {
-    const char* const tr_base =
-        reinterpret_cast<const char*>(&lds.vc[vbuf][dq][tr_entry * VCROWU]) + 8 * ((lane >> 4) & 1);
-    const _Float16* const fac_base = reinterpret_cast<const _Float16*>(&lds.vf[vbuf][dq][0][8 * hh]);
+    const uint32_t bsb = (uint32_t)(127 + VBIAS - base_prev);
+    const uint32_t s8 = r.sc >> (8 * hh);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const auto c = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i*)(tr_base + 16 * mt));
-      const halfx8 f0 = *reinterpret_cast<const halfx8*>(fac_base + 32 * mt);        // entries 8hh + [0, 8)
-      const halfx8 f1 = *reinterpret_cast<const halfx8*>(fac_base + 32 * mt + 16);   // entries 16 + 8hh + [0, 8)
-      va[0][mt] = codes_to_f16(c[0], f0);
-      va[1][mt] = codes_to_f16(c[1], f1);
+      const floatx16 v = mfma_fp4_fp4(mt < 2 ? r.c0 : r.c1, bid[mt & 1], mt < 2 ? s8 : s8 >> 16, bsb);
+      const uint4 a0 = make_uint4(pack_f16(v[0], v[1]), pack_f16(v[2], v[3]), pack_f16(v[4], v[5]),
+                                  pack_f16(v[6], v[7]));
+      const uint4 a1 = make_uint4(pack_f16(v[8], v[9]), pack_f16(v[10], v[11]), pack_f16(v[12], v[13]),
+                                  pack_f16(v[14], v[15]));
+      oacc[mt] = mfma_f16(a0, pfr[0], oacc[mt]);
+      oacc[mt] = mfma_f16(a1, pfr[1], oacc[mt]);
     }
   };
+
   auto read_pfr = [&](int buf) {
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2)
@@ -390,10 +366,9 @@ __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, in
   };
   // Tile t-1's P(t-1).V(t-1), after the rare max move it may need (decided from
   // every wave's quarter maxima of that tile, visible since the last barrier).
-  auto finish_prev = [&](int pbuf) {
+  auto finish_prev = [&](int pbuf, const Raw& rp) {
     const int4 fl = *reinterpret_cast<const int4*>(&lds.flag[pbuf][0]);
     read_pfr(pbuf);
-    read_vt(pbuf);
     if (fl.x | fl.y | fl.z | fl.w) {          // rare (always after the first tile)
       const float tmax = fmaxf(fmaxf(lds.qmax[pbuf][0][e], lds.qmax[pbuf][1][e]),
                                fmaxf(lds.qmax[pbuf][2][e], lds.qmax[pbuf][3][e]));
@@ -412,7 +387,7 @@ __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, in
       read_pfr(pbuf);
     }
     l_lane += (pr_prev[0] + pr_prev[1]) + (pr_prev[2] + pr_prev[3]);
-    issue_pv();
+    issue_pv(rp);
   };
 
   // Pipeline, one barrier per tile.  Tile t, between barriers B(t-1) and B(t)
@@ -422,7 +397,7 @@ __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, in
   //   P(t-1).V(t-1) (after a rare max move) | softmax(t): P(t), flags(t) written
   //   V(t+1) written, Q.K(t+1), S(t+1) partial written
   // S, P, flags and the V tile are double-buffered by tile parity.
-  auto tile_step = [&](int t, Raw& rc, Raw& rl) {
+  auto tile_step = [&](int t, const Raw& rp, Raw& rc, Raw& rl) {
     const int buf = t & 1;
     if (t & 1) __builtin_amdgcn_s_setprio(1);    // wave priority alternates by tile
     else __builtin_amdgcn_s_setprio(0);
@@ -432,7 +407,7 @@ __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, in
     floatx4 sw[4];
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) sw[w2] = lds.sp[buf][w2][dq][lane];
-    if (t > t_begin) finish_prev(buf ^ 1);
+    if (t > t_begin) finish_prev(buf ^ 1, rp);
     int base_next = base_v;
     if (more) base_next = raise_base(rc, base_v);
     floatx4 sq;
@@ -453,20 +428,27 @@ __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, in
     if (lane < 32) lds.qmax[buf][dq][lane] = hmax;
     if (lane == 0) lds.flag[buf][dq] = any_bump;
     sq_prev = sq;
-    base_prev = base_v;           // the base tile t's V was written with
+    base_prev = base_v;           // the base tile t's V is dequantised with
     if (more) {
-      write_vc(buf ^ 1, rc, base_next);
       qk_s(buf ^ 1, rc);
       vmask_cur = (uint32_t)__ballot(rc.valid);
       base_v = base_next;
     }
     __syncthreads();
   };
-  for (int t = t_begin; t < t_end; t += 2) {
-    tile_step(t, ra, rb);
-    if (t + 1 < t_end) tile_step(t + 1, rb, ra);
+  // raw tiles rotate through four register sets: tile t's codes serve Q.K(t)
+  // at step t-1 and P.V(t) at step t+1; step k = t - t_begin: tile t in
+  // R[k % 4], t+1 in R[(k+1) % 4], t+2 arriving in R[(k+2) % 4], t-1 in R[(k+3) % 4]
+  for (int t = t_begin; t < t_end; t += 4) {
+    tile_step(t, rx, ra, rb);
+    if (t + 1 < t_end) tile_step(t + 1, r0, rb, rx);
+    if (t + 2 < t_end) tile_step(t + 2, ra, rx, r0);
+    if (t + 3 < t_end) tile_step(t + 3, rb, r0, ra);
   }
-  if (t_begin < t_end) finish_prev((t_end - 1) & 1);
+  if (t_begin < t_end) {
+    const int k = (t_end - 1 - t_begin) & 3;
+    finish_prev((t_end - 1) & 1, k == 0 ? r0 : k == 1 ? ra : k == 2 ? rb : rx);
+  }
 
   // ---- finalize: denominators across the 4 quarter owners -----------------
   const float lq = pair_sum(l_lane);
