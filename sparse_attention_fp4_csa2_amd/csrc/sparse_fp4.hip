@@ -343,9 +343,12 @@ __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, in
     }
     const uint32_t bsb = (uint32_t)(127 + VBIAS - base_prev);
     const uint32_t s8 = r.sc >> (8 * hh);
+    // two dequantising MFMAs in flight: mt + 1's runs while mt's result is packed
+    floatx16 vn = mfma_fp4_fp4(r.c0, bid[0], s8, bsb);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const floatx16 v = mfma_fp4_fp4(mt < 2 ? r.c0 : r.c1, bid[mt & 1], mt < 2 ? s8 : s8 >> 16, bsb);
+      const floatx16 v = vn;
+      if (mt < 3) vn = mfma_fp4_fp4(mt + 1 < 2 ? r.c0 : r.c1, bid[(mt + 1) & 1], mt + 1 < 2 ? s8 : s8 >> 16, bsb);
       const uint4 a0 = make_uint4(pack_f16(v[0], v[1]), pack_f16(v[2], v[3]), pack_f16(v[4], v[5]),
                                   pack_f16(v[6], v[7]));
       const uint4 a1 = make_uint4(pack_f16(v[8], v[9]), pack_f16(v[10], v[11]), pack_f16(v[12], v[13]),
