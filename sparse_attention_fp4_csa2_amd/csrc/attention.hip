@@ -19,7 +19,10 @@ namespace csa2 {
 
 __global__ __launch_bounds__(256, 2) void window_kernel(AttnParams p, int hgroups) {
   __shared__ win::WinLds lds;
-  win::window_body(p, hgroups, blockIdx.x, lds);
+  int unit, hgi;
+  map_unit(blockIdx.x, p.rows * p.splits, hgroups, p.splits > 1, unit, hgi);
+  if (unit >= p.rows * p.splits) return;
+  win::window_unit(p, unit / p.splits, unit % p.splits, hgi, lds);
 }
 
 int window_splits(int rows, int H, int n_tiles) {

@@ -97,4 +97,25 @@ __device__ __forceinline__ void store_o16_slice(const floatx16 (&acc)[4], float 
   }
 }
 
+// Workgroup L of an attention grid -> (unit, head group), unit = row * splits
+// + split.  With several splits XCD x (= L % 8) runs the x-th contiguous
+// eighth of the (unit, head group) order, so a row's splits and head groups
+// share one XCD's L2 (the row's query comes from HBM once, and the two head
+// groups of a split, dispatched together, share their reads).  With one split
+// (many rows per sequence, as in prefill) unit u goes to XCD u % 8 and its
+// head groups to ids 8 apart: measured to fetch a quarter of the L2 misses of
+// the contiguous order there.
+__device__ __forceinline__ void map_unit(int L, int n_units, int hgroups, bool several_splits, int& unit,
+                                         int& hgi) {
+  if (several_splits) {
+    const int per_xcd = ((n_units + 7) / 8) * hgroups;
+    const int u = (L & 7) * per_xcd + (L >> 3);
+    unit = u / hgroups;
+    hgi = u - unit * hgroups;
+  } else {
+    unit = (L / (8 * hgroups)) * 8 + (L & 7);
+    hgi = (L >> 3) % hgroups;
+  }
+}
+
 }  // namespace csa2

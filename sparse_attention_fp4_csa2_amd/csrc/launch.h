@@ -62,9 +62,11 @@ int launch_window(const AttnParams& p, hipStream_t stream);
 // MXFP4 selected blocks (sparse_fp4.hip): 32-head workgroups, two per CU
 int sparse_fp4_splits(int rows, int H, int n_tiles);
 int launch_sparse_fp4(const AttnParams& p, hipStream_t stream);
-// Both branches of a layer in one launch (sparse_fp4.hip): the sparse
-// workgroups, then the window's; each writes its own partial splits.
-int launch_attend(const AttnParams& ps, const AttnParams& pw, hipStream_t stream);
+// Both branches of a layer in one launch (sparse_fp4.hip); each writes its own
+// partial splits.  inline_window: every sparse workgroup also runs the window
+// split of its own index (needs pw.splits <= ps.splits, same rows and heads);
+// otherwise the window's workgroups follow the sparse ones in the grid.
+int launch_attend(const AttnParams& ps, const AttnParams& pw, bool inline_window, hipStream_t stream);
 
 // Merge split partials (fp16 o, exponent, lse; and an optional fp32 extra
 // branch) -> out [rows][H][512], lse [rows][H].

@@ -129,30 +129,8 @@ constexpr int BUF_DWORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
 
 }  // namespace
 
-// One workgroup's share; L = its index within the sparse grid
-__device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, int hgroups, int L, Lds& lds) {
-  // ---- workgroup -> (row, split, head group), XCD-aware ------------------
-  // With several splits, XCD x (= L % 8) runs the x-th contiguous eighth of
-  // the (row, split, head group) order, so a row's splits and head groups
-  // share one XCD's L2: the row's query comes from HBM once, and the two head
-  // groups of a split (ids 8 apart, dispatched together) share their record
-  // reads.  With one split (many rows per sequence, as in prefill) unit u goes
-  // to XCD u % 8 and its head groups to ids 8 apart: measured to fetch a
-  // quarter of the L2 misses of the contiguous order there.
-  int unit, hgi;
-  if (p.splits > 1) {
-    const int per_xcd = ((n_units + 7) / 8) * hgroups;
-    const int u = (L & 7) * per_xcd + (L >> 3);
-    unit = u / hgroups;
-    hgi = u - unit * hgroups;
-  } else {
-    unit = (L / (8 * hgroups)) * 8 + (L & 7);
-    hgi = (L >> 3) % hgroups;
-  }
-  if (unit >= n_units) return;
-  const int row = unit / p.splits;
-  const int split = unit - row * p.splits;
-
+// One workgroup's share: rows `row`, split `split` of p.splits, head group hgi
+__device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int split, int hgi, Lds& lds) {
   const int tid = threadIdx.x;
   const int dq = tid >> 6;        // wave: latent dims [128dq, 128dq + 128)
   const int lane = tid & 63;
@@ -500,21 +478,43 @@ __device__ __forceinline__ void sparse_body(const AttnParams& p, int n_units, in
 
 __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_units, int hgroups) {
   __shared__ Lds lds;
-  sparse_body(p, n_units, hgroups, blockIdx.x, lds);
+  int unit, hgi;
+  map_unit(blockIdx.x, n_units, hgroups, p.splits > 1, unit, hgi);
+  if (unit >= n_units) return;
+  sparse_unit(p, unit / p.splits, unit % p.splits, hgi, lds);
 }
 
-// Both branches of one layer in one launch: the sparse workgroups come first,
-// the window's after them, so the window runs in the slots the sparse
-// workgroups free as they finish (the first of each CU's pair finishes well
-// ahead of the second) instead of after the last of them.
+// Both branches of one layer in one launch, in one of two arrangements:
+//  * inline (pw.splits <= ps.splits): every sparse workgroup (row, split s,
+//    head group) then runs the window's split s of the same row and head
+//    group, when s < pw.splits.  The window work is spread over all the
+//    sparse workgroups, so it adds a few tiles to each of them instead of
+//    running as short workgroups after them.
+//  * after: the grid is the sparse workgroups followed by the window's, so
+//    the window runs in the slots the sparse workgroups free as they finish.
 __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_units, int hgroups,
-                                                        int n_sparse_wg, AttnParams pw, int whgroups) {
+                                                        int n_sparse_wg, AttnParams pw, int whgroups,
+                                                        int inline_window) {
   __shared__ union {
     Lds s;
     win::WinLds w;
   } lds;
-  if ((int)blockIdx.x < n_sparse_wg) sparse_body(ps, n_units, hgroups, blockIdx.x, lds.s);
-  else win::window_body(pw, whgroups, (int)blockIdx.x - n_sparse_wg, lds.w);
+  int unit, hgi;
+  if ((int)blockIdx.x < n_sparse_wg) {
+    map_unit(blockIdx.x, n_units, hgroups, ps.splits > 1, unit, hgi);
+    if (unit >= n_units) return;
+    const int row = unit / ps.splits, split = unit - row * ps.splits;
+    sparse_unit(ps, row, split, hgi, lds.s);
+    if (inline_window && split < pw.splits) {
+      __syncthreads();                      // the window reuses the LDS
+      win::window_unit(pw, row, split, hgi, lds.w);
+    }
+  } else {
+    const int wn = pw.rows * pw.splits;
+    map_unit((int)blockIdx.x - n_sparse_wg, wn, whgroups, pw.splits > 1, unit, hgi);
+    if (unit >= wn) return;
+    win::window_unit(pw, unit / pw.splits, unit % pw.splits, hgi, lds.w);
+  }
 }
 
 int sparse_fp4_splits(int rows, int H, int n_tiles) {
@@ -540,15 +540,16 @@ int launch_sparse_fp4(const AttnParams& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int launch_attend(const AttnParams& ps, const AttnParams& pw, hipStream_t stream) {
+int launch_attend(const AttnParams& ps, const AttnParams& pw, bool inline_window, hipStream_t stream) {
   const int hgroups = (ps.H + 31) / 32;
   const int n_units = ps.rows * ps.splits;
   const long long n_sparse = (long long)((n_units + 7) / 8) * 8 * hgroups;   // a multiple of 8
   const int whgroups = (pw.H + 31) / 32;
-  const long long n_window = (long long)((pw.rows * pw.splits + 7) / 8) * 8 * whgroups;
+  if (inline_window && (pw.splits > ps.splits || whgroups != hgroups || pw.rows != ps.rows)) return -4;
+  const long long n_window = inline_window ? 0 : (long long)((pw.rows * pw.splits + 7) / 8) * 8 * whgroups;
   if (n_sparse + n_window > 0x7FFFFFFF) return -4;
   attend_kernel<<<dim3((unsigned)(n_sparse + n_window)), 256, 0, stream>>>(ps, n_units, hgroups, (int)n_sparse,
-                                                                           pw, whgroups);
+                                                                           pw, whgroups, inline_window ? 1 : 0);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -74,26 +74,8 @@ struct WinRaw {
   uint4 k[8];      // dims 128dq + 64hh + 8s + [0, 8) of token e, s < 8
 };
 
-__device__ __forceinline__ void window_body(const AttnParams& p, int hgroups, int L, WinLds& lds) {
-  // ---- workgroup -> (row, split, head group), as in the sparse kernel: with
-  // several splits XCD x (= L % 8) runs the x-th contiguous eighth of that
-  // order (a row's query and, between its head groups, its window rows come
-  // from HBM once), with one split unit u goes to XCD u % 8
-  const int n_units = p.rows * p.splits;
-  int unit, hgi;
-  if (p.splits > 1) {
-    const int per_xcd = ((n_units + 7) / 8) * hgroups;
-    const int u = (L & 7) * per_xcd + (L >> 3);
-    unit = u / hgroups;
-    hgi = u - unit * hgroups;
-  } else {
-    unit = (L / (8 * hgroups)) * 8 + (L & 7);
-    hgi = (L >> 3) % hgroups;
-  }
-  if (unit >= n_units) return;
-  const int row = unit / p.splits;
-  const int split = unit - row * p.splits;
-
+// One workgroup's share: row `row`, split `split` of p.splits, head group hgi
+__device__ __forceinline__ void window_unit(const AttnParams& p, int row, int split, int hgi, WinLds& lds) {
   const int tid = threadIdx.x;
   const int dq = tid >> 6;        // wave: latent dims [128dq, 128dq + 128)
   const int lane = tid & 63;

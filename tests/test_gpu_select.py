@@ -28,8 +28,8 @@ def gpu_topk(scores, k):
     return host(idx), host(cnt)
 
 
-@pytest.mark.parametrize("n,k", [(256, 32), (4096, 2048), (8448, 2048), (16384, 2048), (37, 64),
-                                 (1000, 1), (65536, 2048)])
+@pytest.mark.parametrize("n,k", [(256, 32), (4096, 2048), (2502, 700), (8448, 2048), (16384, 2048),
+                                 (37, 64), (1000, 1), (65536, 2048)])
 def test_topk_from_scores_bit_exact_with_ties(n, k):
     rng = rng_for(n * 7 + k)
     rows = 10
