@@ -252,18 +252,24 @@ int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa
 }
 
 // Window splits of a layer, shared by csa2_attend_layer and its two phases so
-// that they write one split layout.  When the sparse branch has at least one
-// split per window tile (few rows: 8 decode rows over 1M-entry caches take 32
-// sparse splits), the window takes one tile per split and every sparse
-// workgroup of the one launch runs the window split of its own index
-// (measured there: 41.0 -> 37.3 us); otherwise the window keeps its own split count and its own
-// workgroups, after the sparse ones (running it inline there cost 5-10 us,
-// since a window split's few tiles are mostly load latency).
+// that they write one split layout.  The window runs inside the sparse
+// workgroups of the one launch (split s of each row and head group in the
+// sparse workgroup of split s) when the sparse branch has at least one split
+// per window tile (few rows: 8 decode rows over 1M-entry caches take 32
+// sparse splits; measured there 36.4 -> 34.3 us) or when the window's own
+// workgroups would each run more than 8 tiles, a long tail after the sparse
+// ones (128 rows of 4 per sequence: 334.6 -> 326.5 us).  Otherwise it keeps
+// its own split count and workgroups after the sparse ones: inline it cost
+// up to ~1 us more there, plus a combine over more splits.
+static bool layer_window_inline(int rows, int H, int s_sparse, int W) {
+  const int wt = (W + 31) / 32;
+  const int s_own = window_splits(rows, H, wt);
+  return s_sparse >= wt || (wt + s_own - 1) / s_own > 8;
+}
 static int layer_window_splits(int rows, int H, int s_sparse, int W) {
   const int wt = (W + 31) / 32;
-  return s_sparse >= wt ? wt : window_splits(rows, H, wt);
+  return layer_window_inline(rows, H, s_sparse, W) ? (s_sparse < wt ? s_sparse : wt) : window_splits(rows, H, wt);
 }
-static bool layer_window_inline(int s_sparse, int W) { return s_sparse >= (W + 31) / 32; }
 
 size_t csa2_attend_layer_ws(int B, int Q, int H, int top_k, int W) {
   if (B <= 0 || Q <= 0 || H <= 0 || top_k <= 0 || W <= 0) return 0;
@@ -364,7 +370,7 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
   pw.cache = nullptr; pw.idx = nullptr; pw.count = nullptr; pw.n_entries = nullptr;
   pw.swa = swa_kv; pw.swa_len = swa_len; pw.swa_pos0 = swa_pos0; pw.W = W; pw.Lw = Lw;
   pw.splits = s_window; pw.split_base = s_sparse;
-  int rc = launch_attend(p, pw, layer_window_inline(s_sparse, W), st);   // both branches in one launch
+  int rc = launch_attend(p, pw, layer_window_inline(rows, H, s_sparse, W), st);   // both branches in one launch
   if (!rc) rc = combine_partials(ws, l, rows, total, H, nullptr, nullptr, out, lse_out, st);
   return launch_status(rc);
 }
