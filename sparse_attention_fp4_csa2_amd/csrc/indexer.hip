@@ -120,14 +120,19 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
 }
 
 // Many query rows of one sequence (chunked prefill): the entry scores are a
-// [rows*Hi x 64] x [64 x N] contraction, done 16 rows at a time on
-// v_mfma_f32_32x32x16_bf16 -- A = 32 (row, head) pairs of a wave (4 rows x 8
-// heads), B = 32 keys -- so each key read from L2 serves 16 rows.  Epilogue as
-// above: ReLU, weights, head sum (lane pair l, l^32), causal mask per row,
-// 8-entry block max.  grid: (entry chunks of CH_ROWS, row tiles of 16 within
-// a sequence); Hi <= 8.
-constexpr int ROWS_T = 16;
-constexpr int CH_ROWS = 4096;
+// [rows*Hi x 64] x [64 x N] contraction on v_mfma_f32_32x32x16_bf16.  A wave
+// holds 16 rows as four A sets of 32 (row, head) pairs (4 rows x 8 heads) and
+// streams 32 keys at a time as B, so each key it loads serves 16 rows, and
+// the 4 waves of a workgroup (64 rows) read the same keys through L1.
+// Epilogue per A set: ReLU and weights over the lane's 4 heads of each row,
+// then one lane swap per row pair (l, l^32) completes the head sums of rows
+// {0, 1} in the low half and {2, 3} in the high one; causal mask per row;
+// 8-entry block max in three DPP steps.  grid: (row tiles of 64, entry chunks
+// of CH_ROWS): the workgroups resident at a time share a few key chunks in
+// L2.  Hi <= 8.
+constexpr int ROWS_W = 16;              // rows per wave
+constexpr int ROWS_T = 4 * ROWS_W;      // rows per workgroup
+constexpr int CH_ROWS = 2048;
 
 __device__ __forceinline__ floatx16 mfma32_bf16(uint4 a, uint4 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -137,39 +142,42 @@ __global__ __launch_bounds__(256) void index_rows_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ key_cache, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ q_pos, int Q, int Hi, int cap, int n_out, float* __restrict__ scores) {
-  const int chunk = blockIdx.x, rt = blockIdx.y;
+  const int rt = blockIdx.x, chunk = blockIdx.y;
   const int tiles_per_seq = (Q + ROWS_T - 1) / ROWS_T;
   const int b = rt / tiles_per_seq;
-  const int q0 = (rt - b * tiles_per_seq) * ROWS_T + 4 * (threadIdx.x >> 6);   // this wave's first row
+  const int q0 = (rt - b * tiles_per_seq) * ROWS_T + ROWS_W * (threadIdx.x >> 6);   // this wave's first row
   const int lane = threadIdx.x & 63;
   const int col = lane & 31, hh = lane >> 5;
   const int ne = min(n_entries[b], cap);
 
-  // A: pair col = (row q0 + col/8, head col%8), dims 16ks + 8hh + [0, 8)
-  uint4 qa[4];
-  {
-    const int r = q0 + (col >> 3), h = col & 7;
+  // A set a: pair col = (row q0 + 4a + col/8, head col%8), dims 16ks + 8hh + [0, 8)
+  uint4 qa[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int r = q0 + 4 * a + (col >> 3), h = col & 7;
     const bool ok = r < Q && h < Hi;
-    const uint16_t* src = q_idx + (((size_t)b * Q + r) * Hi + h) * DI + 8 * hh;
+    const uint16_t* src = q_idx + (((size_t)b * Q + (ok ? r : 0)) * Hi + (ok ? h : 0)) * DI + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      qa[ks] = ok ? *reinterpret_cast<const uint4*>(src + 16 * ks) : make_uint4(0, 0, 0, 0);
+      qa[a][ks] = ok ? *reinterpret_cast<const uint4*>(src + 16 * ks) : make_uint4(0, 0, 0, 0);
   }
-  // accumulator value i: row q0 + i/4, head 4hh + i%4
-  float wv[16];
-  int lim[4];
+  // accumulator value i of set a: row q0 + 4a + i/4, head 4hh + i%4
+  float wv[4][16];
+  int lim[16];
   int lim_max = 0;
 #pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4) {
-    const int r = q0 + r4;
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int h = 4 * hh + k;
-      wv[4 * r4 + k] = (r < Q && h < Hi) ? w[((size_t)b * Q + r) * Hi + h] : 0.f;
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int r = q0 + 4 * a + r4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int h = 4 * hh + k;
+        wv[a][4 * r4 + k] = (r < Q && h < Hi) ? w[((size_t)b * Q + r) * Hi + h] : 0.f;
+      }
+      lim[4 * a + r4] = r < Q ? (q_pos ? min(ne, (q_pos[(size_t)b * Q + r] + 1) >> 1) : ne) : 0;
+      lim_max = max(lim_max, lim[4 * a + r4]);
     }
-    lim[r4] = r < Q ? (q_pos ? min(ne, (q_pos[(size_t)b * Q + r] + 1) >> 1) : ne) : 0;
-    lim_max = max(lim_max, lim[r4]);
-  }
 
   const int e_begin = chunk * CH_ROWS;
   const int e_end = min(e_begin + CH_ROWS, cap);
@@ -187,25 +195,38 @@ __global__ __launch_bounds__(256) void index_rows_kernel(
   };
   auto score = [&](int e, const uint4 (&kv)[4]) {
     const int j = e + col;
-    floatx16 acc = floatx16{};
-    if (e < lim_max) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma32_bf16(qa[ks], kv[ks], acc);
-    }
+    for (int a = 0; a < 4; ++a) {
+      floatx16 acc = floatx16{};
+      if (e < lim_max) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      float s = 0.f;
+        for (int ks = 0; ks < 4; ++ks) acc = mfma32_bf16(qa[a][ks], kv[ks], acc);
+      }
+      // this lane's heads 4hh..4hh+3 of the set's rows r4 = 0..3
+      float ps[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) s += wv[4 * r4 + k] * fmaxf(acc[4 * r4 + k], 0.f);
-      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-      s = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);          // heads 0-3 + 4-7
-      s = j < lim[r4] ? s : -__builtin_inff();
-      s = fmaxf(s, __shfl_xor(s, 1, 64));
-      s = fmaxf(s, __shfl_xor(s, 2, 64));
-      s = fmaxf(s, __shfl_xor(s, 4, 64));
-      const int r = q0 + r4;
-      if (hh == 0 && (col & 7) == 0 && r < Q && j < cap)
-        scores[((size_t)b * Q + r) * n_out + (j >> 3)] = s;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s += wv[a][4 * r4 + k] * fmaxf(acc[4 * r4 + k], 0.f);
+        ps[r4] = s;
+      }
+      // the low lane finishes rows 0, 1 and the high lane rows 2, 3: each sends
+      // its partial sums of the other's rows (swap: [0] = low lane's, [1] = high's)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float snd = hh ? ps[u] : ps[2 + u];
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(snd), __float_as_uint(snd), false, false);
+        const int r4 = 2 * hh + u;
+        float s = (hh ? ps[2 + u] : ps[u]) + __uint_as_float(hh ? pr[0] : pr[1]);
+        s = j < lim[4 * a + r4] ? s : -__builtin_inff();
+        // max over the 8 lanes of the block: quad xor 1, quad xor 2, half-row mirror
+        s = fmaxf(s, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false)));
+        s = fmaxf(s, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false)));
+        s = fmaxf(s, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x141, 0xF, 0xF, false)));
+        const int r = q0 + 4 * a + r4;
+        if ((col & 7) == 0 && r < Q && j < cap) scores[((size_t)b * Q + r) * n_out + (j >> 3)] = s;
+      }
     }
   };
   uint4 k0[4], k1[4];
@@ -272,9 +293,9 @@ int launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k
     index_scores_kernel<CH_GROUP><<<grid, 256, 0, stream>>>(
         q_idx, w, key_cache, n_entries, q_pos, Q, Hi, cap, gsel, n_groups_sel,
         n_groups_sel * (CH_GROUP / BLOCK), scores);
-  } else if (Q >= ROWS_T && Hi <= 8) {
-    // many rows per sequence: 16 rows share each key read
-    dim3 grid((cap + CH_ROWS - 1) / CH_ROWS, B * ((Q + ROWS_T - 1) / ROWS_T));
+  } else if (Q >= 16 && Hi <= 8) {
+    // many rows per sequence: up to 64 rows share each key read
+    dim3 grid(B * ((Q + ROWS_T - 1) / ROWS_T), (cap + CH_ROWS - 1) / CH_ROWS);
     index_rows_kernel<<<grid, 256, 0, stream>>>(q_idx, w, key_cache, n_entries, q_pos, Q, Hi, cap,
                                                 cap / BLOCK, scores);
   } else {

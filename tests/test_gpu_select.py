@@ -173,13 +173,15 @@ def test_two_level_small_bit_exact_and_all_groups_equals_flat():
     assert np.array_equal(got_all, got_flat) and np.array_equal(cnt_all, cnt_flat)
 
 
-@pytest.mark.parametrize("hi", [8, 5])
-def test_many_rows_per_sequence_scores_and_selection(hi):
-    # 40 causal query rows per sequence (two full 16-row tiles and a ragged one),
-    # the multi-row MFMA indexer; block scores compared value by value
-    B, Q, cap, K = 2, 40, 4096 + 512, 64
+@pytest.mark.parametrize("hi,Q", [(8, 40), (5, 40), (8, 150)])
+def test_many_rows_per_sequence_scores_and_selection(hi, Q):
+    # causal query rows of the multi-row MFMA indexer (64-row workgroups of four
+    # 16-row waves): 40 rows leave one wave partly filled and one empty, 150
+    # rows take two full workgroups and a ragged third; block scores compared
+    # value by value
+    B, cap, K = 2, 4096 + 512, 64
     cfg = Config("m", B=B, Q=Q, H=16, N=cap, Hi=hi, K=K, W=16, seed=21)
-    rng = rng_for(21 + hi)
+    rng = rng_for(21 + hi + Q)
     keys = normal_bf16(rng, (B, cap, 64))
     q_idx = normal_bf16(rng, (B, Q, hi, 64))
     w = rng.standard_normal((B, Q, hi)).astype(np.float32)
