@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
 // L2.  Hi <= 8.
 constexpr int ROWS_W = 16;              // rows per wave
 constexpr int ROWS_T = 4 * ROWS_W;      // rows per workgroup
-constexpr int CH_ROWS = 2048;
+constexpr int CH_ROWS = 1024;     // 64 row tiles x 66 chunks at prefill: 8+ rounds of 512 slots
 
 __device__ __forceinline__ floatx16 mfma32_bf16(uint4 a, uint4 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
