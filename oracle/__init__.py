@@ -12,6 +12,8 @@ each step so it can be checked against the pages by eye:
 * ``bf16``      -- bit-level bfloat16 <-> float64 (input decoding only).
 * ``mxfp4``     -- MXFP4 (FP4 E2M1 codes + one E8M0 scale per 32 values) encode,
                    decode and the block-record byte layout of the global cache.
+* ``mxfp8``     -- MXFP8 (E4M3 codes + one E8M0 scale per 32 values) encode and
+                   decode of the indexer keys (the lower-precision key cache).
 * ``indexer``   -- entry/block scores of the sparse indexer and the two-level
                    (hierarchical) group stage.
 * ``topk``      -- top-K block selection with its tie rule and output order.
@@ -39,4 +41,4 @@ Parity-pin status: every public function is pinned by tests under ``tests/``
 (closed forms, brute force, special cases, invariants); none is "parity unpinned".
 """
 
-from . import bf16, mxfp4, indexer, topk, attention, modes  # noqa: F401
+from . import bf16, mxfp4, mxfp8, indexer, topk, attention, modes  # noqa: F401
