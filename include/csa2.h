@@ -99,6 +99,34 @@ int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* key_c
                     int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_index_topk_ws(int B, int Q, int cap, int top_groups);
 
+/* Lower-precision indexer key cache: the keys in MXFP8 (OCP Microscaling
+ * v1.0, E4M3 elements -- bias 7, subnormals, largest finite 448, no
+ * infinities -- with one E8M0 scale per 32 dims), half the bytes of bf16.
+ * The pages give the indexer no precision (observer.broadside.tech card, Key
+ * ideas, "CSA2 with three static layer modes"); the latent stays MXFP4.
+ * Encoding of a 32-dim group x: sb = clamp(floor(log2 max|x|) - 8 + 127, 0,
+ * 254) (0 for an all-zero group), code = sign<<7 | E4M3 magnitude of
+ * |x| / 2^(sb-127) rounded to nearest, ties to the even code, above 448
+ * saturating to 448 (0x7E).
+ *
+ * csa2_append_key8: quantises n_new new keys per sequence (bf16 idx_key
+ * [B][n_new][64]) into entries start_entry[b] .. of key8 u8 [B][cap][64]
+ * (byte d = dim d; 16-B aligned) and key8_scale u8 [B][cap][2] (byte g for
+ * dims 32g..32g+31; 4-B aligned), and adds the dequantised keys to group_sum
+ * fp32 [B][cap/512][64] when it is not NULL (cap % 512 == 0).  Pair it with
+ * csa2_append_fp4(..., idx_key = NULL, key_cache = NULL, group_sum = NULL)
+ * for the latent.  Entries at or beyond cap are skipped.
+ *
+ * csa2_index_topk_key8: csa2_index_topk on such a cache (the scores use the
+ * dequantised keys, exact in bf16, against the bf16 query); same outputs,
+ * workspace (csa2_index_topk_ws) and errors. */
+int csa2_append_key8(const uint16_t* idx_key, const int32_t* start_entry, int B, int n_new, int cap,
+                     uint8_t* key8, uint8_t* key8_scale, float* group_sum, void* stream);
+int csa2_index_topk_key8(const uint16_t* q_idx, const float* w, const uint8_t* key8,
+                         const uint8_t* key8_scale, const float* group_sum, const int32_t* n_entries,
+                         const int32_t* q_pos, int B, int Q, int Hi, int cap, int top_k, int top_groups,
+                         int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
+
 /* Top-K of precomputed scores (the selection step of csa2_index_topk).
  * scores fp32 [rows][n]; -inf or NaN marks a non-candidate.  Same rule and
  * output format as csa2_index_topk: idx int32 [rows][k] ascending, -1 padded;

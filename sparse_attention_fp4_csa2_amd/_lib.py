@@ -26,6 +26,8 @@ _SIGS = {
     "csa2_append_fp4": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
     "csa2_index_topk": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "csa2_index_topk_ws": (_SZ, [_I, _I, _I, _I]),
+    "csa2_append_key8": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _P]),
+    "csa2_index_topk_key8": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "csa2_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "csa2_sparse_attn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]),
     "csa2_sparse_attn_ws": (_SZ, [_I, _I, _I, _I]),
@@ -131,6 +133,34 @@ def index_topk(q_idx, w, key_cache, n_entries, top_k, idx, count, ws, group_sum=
                              _ptr(idx, torch.int32, "idx"), _ptr(count, torch.int32, "count"),
                              _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "csa2_index_topk")
+
+
+def append_key8(idx_key, start_entry, key8, key8_scale, group_sum=None, stream=None):
+    """csa2_append_key8: keys bf16 [B][n_new][64] -> key8 u8 [B][cap][64], key8_scale u8 [B][cap][2]."""
+    lib = load()
+    B, n_new = idx_key.shape[0], idx_key.shape[1]
+    cap = key8.shape[1]
+    rc = lib.csa2_append_key8(_bf16_ptr(idx_key, "idx_key"), _ptr(start_entry, torch.int32, "start_entry"),
+                              B, n_new, cap, _ptr(key8, torch.uint8, "key8"),
+                              _ptr(key8_scale, torch.uint8, "key8_scale"),
+                              _ptr(group_sum, torch.float32, "group_sum"), _stream(stream))
+    _check(rc, "csa2_append_key8")
+
+
+def index_topk_key8(q_idx, w, key8, key8_scale, n_entries, top_k, idx, count, ws, group_sum=None,
+                    q_pos=None, top_groups=0, stream=None):
+    """csa2_index_topk_key8: as index_topk, on an MXFP8 key cache (key8, key8_scale)."""
+    lib = load()
+    B, Q, Hi = q_idx.shape[0], q_idx.shape[1], q_idx.shape[2]
+    cap = key8.shape[1]
+    rc = lib.csa2_index_topk_key8(_bf16_ptr(q_idx, "q_idx"), _ptr(w, torch.float32, "w"),
+                                  _ptr(key8, torch.uint8, "key8"), _ptr(key8_scale, torch.uint8, "key8_scale"),
+                                  _ptr(group_sum, torch.float32, "group_sum"),
+                                  _ptr(n_entries, torch.int32, "n_entries"), _ptr(q_pos, torch.int32, "q_pos"),
+                                  B, Q, Hi, cap, top_k, top_groups,
+                                  _ptr(idx, torch.int32, "idx"), _ptr(count, torch.int32, "count"),
+                                  _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "csa2_index_topk_key8")
 
 
 def topk(scores, k, idx, count, stream=None):

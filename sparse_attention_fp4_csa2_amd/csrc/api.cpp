@@ -126,15 +126,15 @@ size_t csa2_index_topk_ws(int B, int Q, int cap, int top_groups) {
   return index_ws_layout(B, Q, cap, top_groups).total;
 }
 
-int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* key_cache,
-                    const float* group_sum, const int32_t* n_entries, const int32_t* q_pos,
-                    int B, int Q, int Hi, int cap, int top_k, int top_groups,
-                    int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
-  if (!q_idx || !w || !key_cache || !n_entries || !idx || !count) return CSA2_ERR_INVALID_ARG;
+static int index_topk(const uint16_t* q_idx, const float* w, const KeyCache& keys,
+                      const float* group_sum, const int32_t* n_entries, const int32_t* q_pos,
+                      int B, int Q, int Hi, int cap, int top_k, int top_groups,
+                      int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  if (!q_idx || !w || !n_entries || !idx || !count) return CSA2_ERR_INVALID_ARG;
   if (B <= 0 || Q <= 0 || Hi <= 0 || cap <= 0 || top_k <= 0 || top_groups < 0)
     return CSA2_ERR_INVALID_ARG;
   if (cap % CSA2_BLOCK != 0 || top_k > cap / CSA2_BLOCK) return CSA2_ERR_INVALID_ARG;
-  if (!aligned(q_idx, 16) || !aligned(key_cache, 16)) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q_idx, 16)) return CSA2_ERR_INVALID_ARG;
   if (Hi > CSA2_MAX_INDEX_HEADS) return CSA2_ERR_UNSUPPORTED;
   if ((size_t)cap / CSA2_BLOCK > 65536) return CSA2_ERR_UNSUPPORTED;
   const IndexWs l = index_ws_layout(B, Q, cap, top_groups);
@@ -145,8 +145,7 @@ int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* key_c
   hipStream_t st = as_stream(stream);
   const int rows = B * Q;
   if (top_groups == 0) {
-    int rc = launch_index_scores(q_idx, w, key_cache, n_entries, q_pos, B, Q, Hi, cap, nullptr, 0,
-                                 scores, st);
+    int rc = launch_index_scores(q_idx, w, keys, n_entries, q_pos, B, Q, Hi, cap, nullptr, 0, scores, st);
     if (rc) return CSA2_ERR_LAUNCH;
     return launch_status(launch_topk(scores, rows, cap / CSA2_BLOCK, top_k, nullptr, 0, idx, count, st));
   }
@@ -161,11 +160,47 @@ int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* key_c
   int32_t* gcount = reinterpret_cast<int32_t*>(base + l.gcount);
   int rc = launch_group_scores(q_idx, w, group_sum, n_entries, B, Q, Hi, cap, gscores, st);
   if (!rc) rc = launch_topk(gscores, rows, G, top_groups, nullptr, 0, gsel, gcount, st);
-  if (!rc) rc = launch_index_scores(q_idx, w, key_cache, n_entries, nullptr, B, Q, Hi, cap, gsel,
-                                    top_groups, scores, st);
+  if (!rc) rc = launch_index_scores(q_idx, w, keys, n_entries, nullptr, B, Q, Hi, cap, gsel, top_groups,
+                                    scores, st);
   if (!rc) rc = launch_topk(scores, rows, top_groups * CSA2_GROUP_BLOCKS, top_k, gsel, top_groups,
                             idx, count, st);
   return launch_status(rc);
+}
+
+int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* key_cache,
+                    const float* group_sum, const int32_t* n_entries, const int32_t* q_pos,
+                    int B, int Q, int Hi, int cap, int top_k, int top_groups,
+                    int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  if (!key_cache) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(key_cache, 16)) return CSA2_ERR_INVALID_ARG;
+  const KeyCache keys{key_cache, nullptr, nullptr};
+  return index_topk(q_idx, w, keys, group_sum, n_entries, q_pos, B, Q, Hi, cap, top_k, top_groups, idx,
+                    count, ws, ws_bytes, stream);
+}
+
+int csa2_index_topk_key8(const uint16_t* q_idx, const float* w, const uint8_t* key8,
+                         const uint8_t* key8_scale, const float* group_sum, const int32_t* n_entries,
+                         const int32_t* q_pos, int B, int Q, int Hi, int cap, int top_k, int top_groups,
+                         int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  if (!key8 || !key8_scale) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(key8, 16) || !aligned(key8_scale, 4)) return CSA2_ERR_INVALID_ARG;
+  const KeyCache keys{nullptr, key8, key8_scale};
+  return index_topk(q_idx, w, keys, group_sum, n_entries, q_pos, B, Q, Hi, cap, top_k, top_groups, idx,
+                    count, ws, ws_bytes, stream);
+}
+
+int csa2_append_key8(const uint16_t* idx_key, const int32_t* start_entry, int B, int n_new, int cap,
+                     uint8_t* key8, uint8_t* key8_scale, float* group_sum, void* stream) {
+  if (!idx_key || !start_entry || !key8 || !key8_scale) return CSA2_ERR_INVALID_ARG;
+  if (B <= 0 || n_new < 0 || cap <= 0 || cap % CSA2_BLOCK != 0) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(key8, 16) || !aligned(key8_scale, 4)) return CSA2_ERR_INVALID_ARG;
+  if (group_sum) {
+    if (cap % 512 != 0) return CSA2_ERR_UNSUPPORTED;
+    if (!aligned(group_sum, 16)) return CSA2_ERR_INVALID_ARG;
+  }
+  if (n_new == 0) return CSA2_OK;
+  return launch_status(launch_append_key8(idx_key, start_entry, B, n_new, cap, key8, key8_scale, group_sum,
+                                          as_stream(stream)));
 }
 
 int csa2_topk(const float* scores, int rows, int n, int k, int32_t* idx, int32_t* count,

@@ -9,7 +9,9 @@
 //
 // The entry scores are a genuine [Hi x 64] x [64 x N] contraction per query
 // row, done on v_mfma_f32_16x16x32_bf16: A = the row's indexer query (heads
-// padded to 16), B = 16 keys per MFMA.  The ReLU, weights, head sum and the
+// padded to 16), B = 16 keys per MFMA.  Keys are bf16, or MXFP8 (E4M3 codes
+// with one E8M0 scale per 32 dims) converted to bf16 in registers on load
+// (v_cvt_scalef32_pk_bf16_fp8: exact), which halves the bytes read.  The ReLU, weights, head sum and the
 // 8-entry block max run in the epilogue, so entry scores never reach memory.
 // Keys stream once from HBM with 32-byte loads per lane.
 #include "device.h"
@@ -28,16 +30,33 @@ __device__ __forceinline__ floatx4 mfma16(uint4 a, uint4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// MXFP8 keys: E8M0 scale byte -> the float 2^(sb - 127) (sb = 0: the fp32
+// subnormal 2^-127)
+__device__ __forceinline__ float e8m0_float(uint32_t sb) {
+  return __uint_as_float(sb ? sb << 23 : 1u << 22);
+}
+// 4 E4M3 codes (bytes of c, byte 0 first) times the scale -> 4 bf16 (the
+// products are exact: 4 significant bits times a power of two)
+__device__ __forceinline__ uint2 fp8x4_bf16(uint32_t c, float scale) {
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, true)));
+}
+__device__ __forceinline__ uint4 fp8x8_bf16(uint32_t lo, uint32_t hi, float scale) {
+  const uint2 a = fp8x4_bf16(lo, scale), b = fp8x4_bf16(hi, scale);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
 }  // namespace
 
 // grid: (chunks, rows).  Flat: chunk x covers entries [x*CH, x*CH + CH) and
 // writes block scores at [row][x*CH/8 ...] of a row of length n_out = cap/8.
 // Group-restricted: chunk x covers group gsel[row][x] and writes at
 // [row][x*64 ...] of a row of length n_out = 64 * n_groups_sel.
-template <int CH>
+template <int CH, bool K8>
 __global__ __launch_bounds__(256) void index_scores_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint16_t* __restrict__ key_cache, const int32_t* __restrict__ n_entries,
+    const uint16_t* __restrict__ key_cache, const uint8_t* __restrict__ key8,
+    const uint8_t* __restrict__ key8_scale, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ q_pos, int Q, int Hi, int cap,
     const int32_t* __restrict__ gsel, int n_groups_sel, int n_out, float* __restrict__ scores) {
   const int x = blockIdx.x, row = blockIdx.y;
@@ -81,7 +100,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
   constexpr int PER_WAVE = CH / 4;              // entries per wave
   constexpr int TILES = PER_WAVE / 16;
   const int wbase = e0 + wave * PER_WAVE;
-  const uint16_t* kbase = key_cache + (size_t)b * cap * DI;
+  const uint16_t* kbase = K8 ? nullptr : key_cache + (size_t)b * cap * DI;
 
   for (int t0 = 0; t0 < TILES; t0 += UNROLL) {
     uint4 kb[UNROLL][2];
@@ -89,9 +108,17 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
     for (int u = 0; u < UNROLL; ++u) {
       const int j = wbase + 16 * (t0 + u) + n;
       if (j < jmax) {
-        const uint4* kp = reinterpret_cast<const uint4*>(kbase + (size_t)j * DI + 16 * kg);
-        kb[u][0] = kp[0];
-        kb[u][1] = kp[1];
+        if constexpr (K8) {
+          const size_t ke = (size_t)b * cap + (size_t)j;
+          const uint4 c = *reinterpret_cast<const uint4*>(key8 + ke * DI + 16 * kg);
+          const float sc = e8m0_float(key8_scale[ke * 2 + (kg >> 1)]);
+          kb[u][0] = fp8x8_bf16(c.x, c.y, sc);
+          kb[u][1] = fp8x8_bf16(c.z, c.w, sc);
+        } else {
+          const uint4* kp = reinterpret_cast<const uint4*>(kbase + (size_t)j * DI + 16 * kg);
+          kb[u][0] = kp[0];
+          kb[u][1] = kp[1];
+        }
       } else {
         kb[u][0] = make_uint4(0, 0, 0, 0);
         kb[u][1] = kb[u][0];
@@ -138,9 +165,11 @@ __device__ __forceinline__ floatx16 mfma32_bf16(uint4 a, uint4 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+template <bool K8>
 __global__ __launch_bounds__(256) void index_rows_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint16_t* __restrict__ key_cache, const int32_t* __restrict__ n_entries,
+    const uint16_t* __restrict__ key_cache, const uint8_t* __restrict__ key8,
+    const uint8_t* __restrict__ key8_scale, const int32_t* __restrict__ n_entries,
     const int32_t* __restrict__ q_pos, int Q, int Hi, int cap, int n_out, float* __restrict__ scores) {
   const int rt = blockIdx.x, chunk = blockIdx.y;
   const int tiles_per_seq = (Q + ROWS_T - 1) / ROWS_T;
@@ -181,13 +210,25 @@ __global__ __launch_bounds__(256) void index_rows_kernel(
 
   const int e_begin = chunk * CH_ROWS;
   const int e_end = min(e_begin + CH_ROWS, cap);
-  const uint16_t* kbase = key_cache + (size_t)b * cap * DI + 8 * hh;
+  const uint16_t* kbase = K8 ? nullptr : key_cache + (size_t)b * cap * DI + 8 * hh;
   auto load = [&](int e, uint4 (&kv)[4]) {
     const int j = e + col;
     if (j < lim_max) {
-      const uint16_t* kp = kbase + (size_t)j * DI;
+      if constexpr (K8) {
+        // dims 16ks + 8hh + [0, 8): 8 codes at that byte offset, scale of group ks / 2
+        const size_t ke = (size_t)b * cap + (size_t)j;
+        const uint8_t* kp = key8 + ke * DI + 8 * hh;
+        const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(key8_scale + ke * 2);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kv[ks] = *reinterpret_cast<const uint4*>(kp + 16 * ks);
+        for (int ks = 0; ks < 4; ++ks) {
+          const uint2 c = *reinterpret_cast<const uint2*>(kp + 16 * ks);
+          kv[ks] = fp8x8_bf16(c.x, c.y, e8m0_float((sc2 >> (8 * (ks >> 1))) & 0xFFu));
+        }
+      } else {
+        const uint16_t* kp = kbase + (size_t)j * DI;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kv[ks] = *reinterpret_cast<const uint4*>(kp + 16 * ks);
+      }
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kv[ks] = make_uint4(0, 0, 0, 0);
@@ -283,26 +324,39 @@ __global__ __launch_bounds__(256) void group_scores_kernel(
   if (h0 == 0 && g < G) gscores[(size_t)row * G + g] = cnt > 0 ? s : -__builtin_inff();
 }
 
-int launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* key_cache,
-                        const int32_t* n_entries, const int32_t* q_pos, int B, int Q, int Hi,
-                        int cap, const int32_t* gsel, int n_groups_sel, float* scores,
-                        hipStream_t stream) {
+template <bool K8>
+static void launch_index_scores_t(const uint16_t* q_idx, const float* w, const KeyCache& k,
+                                  const int32_t* n_entries, const int32_t* q_pos, int B, int Q, int Hi,
+                                  int cap, const int32_t* gsel, int n_groups_sel, float* scores,
+                                  hipStream_t stream) {
   const int rows = B * Q;
   if (gsel) {
     dim3 grid(n_groups_sel, rows);
-    index_scores_kernel<CH_GROUP><<<grid, 256, 0, stream>>>(
-        q_idx, w, key_cache, n_entries, q_pos, Q, Hi, cap, gsel, n_groups_sel,
+    index_scores_kernel<CH_GROUP, K8><<<grid, 256, 0, stream>>>(
+        q_idx, w, k.bf16, k.codes, k.scales, n_entries, q_pos, Q, Hi, cap, gsel, n_groups_sel,
         n_groups_sel * (CH_GROUP / BLOCK), scores);
   } else if (Q >= 16 && Hi <= 8) {
     // many rows per sequence: up to 64 rows share each key read
     dim3 grid(B * ((Q + ROWS_T - 1) / ROWS_T), (cap + CH_ROWS - 1) / CH_ROWS);
-    index_rows_kernel<<<grid, 256, 0, stream>>>(q_idx, w, key_cache, n_entries, q_pos, Q, Hi, cap,
-                                                cap / BLOCK, scores);
+    index_rows_kernel<K8><<<grid, 256, 0, stream>>>(q_idx, w, k.bf16, k.codes, k.scales, n_entries, q_pos,
+                                                    Q, Hi, cap, cap / BLOCK, scores);
   } else {
     dim3 grid((cap + CH_FLAT - 1) / CH_FLAT, rows);
-    index_scores_kernel<CH_FLAT><<<grid, 256, 0, stream>>>(
-        q_idx, w, key_cache, n_entries, q_pos, Q, Hi, cap, nullptr, 0, cap / BLOCK, scores);
+    index_scores_kernel<CH_FLAT, K8><<<grid, 256, 0, stream>>>(
+        q_idx, w, k.bf16, k.codes, k.scales, n_entries, q_pos, Q, Hi, cap, nullptr, 0, cap / BLOCK, scores);
   }
+}
+
+int launch_index_scores(const uint16_t* q_idx, const float* w, const KeyCache& keys,
+                        const int32_t* n_entries, const int32_t* q_pos, int B, int Q, int Hi,
+                        int cap, const int32_t* gsel, int n_groups_sel, float* scores,
+                        hipStream_t stream) {
+  if (keys.bf16)
+    launch_index_scores_t<false>(q_idx, w, keys, n_entries, q_pos, B, Q, Hi, cap, gsel, n_groups_sel, scores,
+                                 stream);
+  else
+    launch_index_scores_t<true>(q_idx, w, keys, n_entries, q_pos, B, Q, Hi, cap, gsel, n_groups_sel, scores,
+                                stream);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -11,9 +11,21 @@ int launch_append(const uint16_t* latent, const uint16_t* idx_key, const int32_t
                   int B, int n_new, int cap, uint8_t* cache, uint16_t* key_cache,
                   float* group_sum, hipStream_t stream);
 
+// MXFP8 indexer keys (append.hip): E4M3 codes [B][cap][64] + E8M0 scales
+// [B][cap][2]; group sums (optional) of the dequantised keys
+int launch_append_key8(const uint16_t* idx_key, const int32_t* start_entry, int B, int n_new, int cap,
+                       uint8_t* key8, uint8_t* key8_scale, float* group_sum, hipStream_t stream);
+
+// Indexer keys: bf16 [B][cap][64] (bf16 != nullptr) or MXFP8 (codes, scales).
+struct KeyCache {
+  const uint16_t* bf16;
+  const uint8_t* codes;
+  const uint8_t* scales;
+};
+
 // Block scores fp32 [rows][n_out]: flat (gsel == nullptr: n_out = cap/8) or
 // restricted to the selected groups gsel [rows][n_groups_sel] (n_out = 64 per group).
-int launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* key_cache,
+int launch_index_scores(const uint16_t* q_idx, const float* w, const KeyCache& keys,
                         const int32_t* n_entries, const int32_t* q_pos, int B, int Q, int Hi,
                         int cap, const int32_t* gsel, int n_groups_sel, float* scores,
                         hipStream_t stream);
