@@ -75,6 +75,30 @@ def parse(argv=None):
 # workloads (device state + one step), shared with the full-size parity tests
 
 
+class Key8Index:
+    """The same selection on the MXFP8 indexer key cache (csa2_append_key8 +
+    csa2_index_topk_key8): a timed call beside the step, not part of it."""
+
+    def __init__(self, lib, keys, cap, B, Q, K, top_groups, device="cuda"):
+        import torch
+        self.lib, self.K, self.top_groups = lib, K, top_groups
+        self.key8 = torch.zeros(B, cap, 64, dtype=torch.uint8, device=device)
+        self.scale = torch.zeros(B, cap, 2, dtype=torch.uint8, device=device)
+        self.gsum = (torch.zeros(B, cap // 512, 64, dtype=torch.float32, device=device)
+                     if top_groups else None)
+        lib.append_key8(keys, torch.zeros(B, dtype=torch.int32, device=device), self.key8, self.scale,
+                        group_sum=self.gsum)
+        self.idx = torch.empty(B, Q, K, dtype=torch.int32, device=device)
+        self.count = torch.empty(B, Q, dtype=torch.int32, device=device)
+        self.ws = torch.empty(max(lib.index_topk_ws(B, Q, cap, top_groups), 256), dtype=torch.uint8,
+                              device=device)
+
+    def call(self, q_idx, w, n_entries, q_pos, stream):
+        self.lib.index_topk_key8(q_idx, w, self.key8, self.scale, n_entries, self.K, self.idx, self.count,
+                                 self.ws, group_sum=self.gsum, q_pos=q_pos, top_groups=self.top_groups,
+                                 stream=stream)
+
+
 class DecodeWorkload:
     """Decode: B sequences, one query row each, through the layers of ``cfg.layers``."""
 
@@ -87,6 +111,7 @@ class DecodeWorkload:
         self.B, self.rows = B, B * cfg.Q
         self.cache = modes.LatentCache.empty(B, cfg.cap, device, with_groups=bool(cfg.top_groups))
         self.cache.append(_bf(x.latent, device), _bf(x.keys, device))
+        self.key8 = Key8Index(_lib, _bf(x.keys, device), cfg.cap, B, cfg.Q, cfg.K, cfg.top_groups, device)
         self.swa_len = torch.from_numpy(x.swa_len).to(device)
         self.layers = []
         for L in layers:
@@ -134,6 +159,8 @@ class DecodeWorkload:
                              len(self.layers)),
             # the two branches as separate calls (not part of the step; sparse_attn is the roofline unit)
             "sparse_attn": (self.sparse_attn_call, 0),
+            "index_topk_key8": (lambda: self.key8.call(L0["q_idx"], L0["w"], self.cache.n_entries, self.q_pos, s),
+                                0),
             "swa_merge": (lambda: lib.swa_merge(L0["q"], L0["swa"], self.swa_len, self.cfg.W, m.SCALE,
                                                 buf.o, buf.lse, buf.out, buf.lse_out, buf.ws_swa,
                                                 swa_pos0=self.swa_pos0, q_pos=self.q_pos, stream=s), 0),
@@ -165,6 +192,7 @@ class PrefillWorkload:
         self.B, self.rows = 1, Q
         self.cache = modes.LatentCache.empty(1, cfg.cap, device)
         self.cache.append(_bf(p["latent"], device), _bf(p["keys"], device))
+        self.key8 = Key8Index(_lib, _bf(p["keys"], device), cfg.cap, 1, Q, cfg.K, 0, device)
         self.buf = modes.LayerBuffers(1, Q, cfg.H, cfg.cap, cfg.K, cfg.W, device=device)
         self.q = _bf(p["q"], device)
         self.q_idx = _bf(p["q_idx"], device)
@@ -210,7 +238,9 @@ class PrefillWorkload:
     def calls(self):
         return {"append": (self.append, 1), "index_topk": (self.index, 1),
                 "attend_layer": (self.attend_call, 1),
-                "sparse_attn": (self.sparse_attn_call, 0), "swa_merge": (self.swa_call, 0)}
+                "sparse_attn": (self.sparse_attn_call, 0), "swa_merge": (self.swa_call, 0),
+                "index_topk_key8": (lambda: self.key8.call(self.q_idx, self.w, self.cache.n_entries, self.q_pos,
+                                                           self.stream), 0)}
 
     def attended_entries(self):
         """Visible entries of the selected blocks summed over rows (causal masking counted)."""
@@ -373,6 +403,10 @@ def main():
         idx_bytes = wl.B * cfg.N * 128 if not cfg.top_groups else \
             wl.B * (cfg.cap // 512 * 256 + cfg.top_groups * 512 * 128)
         result["indexer_GBps"] = round(idx_bytes / (breakdown["index_topk"] * 1e-3) / 1e9, 1)
+        # the same call on the MXFP8 key cache: 64 code bytes + 2 scale bytes per key
+        idx8_bytes = wl.B * cfg.N * 66 if not cfg.top_groups else \
+            wl.B * (cfg.cap // 512 * 256 + cfg.top_groups * 512 * 66)
+        result["indexer_key8_GBps"] = round(idx8_bytes / (breakdown["index_topk_key8"] * 1e-3) / 1e9, 1)
     if len(cfg.layers) > 1:
         result["reuse_saving_ms"] = round(breakdown["index_topk"] * cfg.layers.count("U"), 4)
 
