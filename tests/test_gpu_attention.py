@@ -265,12 +265,13 @@ def test_repeat_runs_bitwise_identical():
         assert o.tobytes() == outs[0][0].tobytes() and l.tobytes() == outs[0][1].tobytes()
 
 
-def gpu_layer(q, cache, idx, count, n_entries, swa, swa_len, W, swa_pos0=None, q_pos=None):
+def gpu_layer(q, cache, idx, count, n_entries, swa, swa_len, W, swa_pos0=None, q_pos=None, ws=None):
     lib = _lib()
     B, Q, H = q.shape[:3]
     out = torch.full((B, Q, H, 512), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.full((B, Q, H), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(lib.attend_layer_ws(B, Q, H, idx.shape[-1], W), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws = torch.empty(lib.attend_layer_ws(B, Q, H, idx.shape[-1], W), dtype=torch.uint8, device="cuda")
     lib.attend_layer(dev_bf16(q), cache, dev(np.ascontiguousarray(idx, np.int32)),
                      dev(np.asarray(count, np.int32)), dev(np.asarray(n_entries, np.int32)), dev_bf16(swa),
                      dev(np.asarray(swa_len, np.int32)), W, SCALE, out, lse, ws,
@@ -366,6 +367,31 @@ def test_two_phase_layer_on_two_streams_matches_one_call():
         torch.cuda.synchronize()
         assert np.array_equal(host(out), ref_o), f"call {call}: out differs from csa2_attend_layer"
         assert np.array_equal(host(lse), ref_l), f"call {call}: lse differs from csa2_attend_layer"
+
+
+@pytest.mark.parametrize("B,H", [(2, 64), (8, 40)])
+def test_one_launch_layer_reuses_its_workspace(B, H):
+    # the library keeps no state between calls: three calls in a row on one
+    # workspace (other queries, the last with fewer rows) give the bytes of
+    # calls on fresh workspaces.  B = 8 puts the window inside the sparse
+    # workgroups; H = 40 leaves a partly filled head group.
+    lib = _lib()
+    rng = rng_for(61 + B)
+    Q, N, K, W, Lw = 1, 8192, 256, 128, 128
+    cache = gpu_cache(normal_bf16(rng, (B, N, 512)), N)
+    swa = normal_bf16(rng, (B, Lw, 512))
+    idx = np.stack([np.sort(rng.choice(N // 8, K, replace=False)) for _ in range(B * Q)]).reshape(B, Q, K)
+    count = np.full((B, Q), K, np.int32)
+    count[0, 0] = 100
+    n_entries = np.full(B, N, np.int32)
+    ws = torch.empty(lib.attend_layer_ws(B, Q, H, K, W), dtype=torch.uint8, device="cuda")
+    for call, b in enumerate((B, B, B - 1)):
+        q = normal_bf16(rng, (b, Q, H, 512))
+        args = (cache[:b], idx[:b].astype(np.int32), count[:b], n_entries[:b], swa[:b], [Lw] * b, W)
+        o1, l1 = gpu_layer(q, *args, ws=ws)
+        o2, l2 = gpu_layer(q, *args)
+        assert np.isfinite(o1).all(), call
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), f"call {call}"
 
 
 def test_run_layer_side_stream_matches_one_stream():
