@@ -60,6 +60,9 @@ def parse(argv=None):
     ap.add_argument("--config", default="decode64k",
                     choices=["tiny", "decode64k", "decode1m", "layers128k", "prefill", "specdec64k"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
+    ap.add_argument("--index-keys", default="bf16", choices=["bf16", "mxfp8"],
+                    help="indexer key cache: bf16 (the workload's definition) or the lower-precision "
+                         "MXFP8 variant")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="reps of the cold timings (a 1 GiB write before each evicts L2 and the 256 MB "
@@ -102,16 +105,18 @@ class Key8Index:
 class DecodeWorkload:
     """Decode: B sequences, one query row each, through the layers of ``cfg.layers``."""
 
-    def __init__(self, cfg, x, layers, device="cuda"):
+    def __init__(self, cfg, x, layers, device="cuda", key_format="bf16"):
         import torch
         from sparse_attention_fp4_csa2_amd import _lib, modes
         self.torch, self._lib, self.modes = torch, _lib, modes
         self.cfg, self.x, self.layer_inputs = cfg, x, layers
         B, N = x.latent.shape[0], cfg.N
         self.B, self.rows = B, B * cfg.Q
-        self.cache = modes.LatentCache.empty(B, cfg.cap, device, with_groups=bool(cfg.top_groups))
+        self.cache = modes.LatentCache.empty(B, cfg.cap, device, with_groups=bool(cfg.top_groups),
+                                             key_format=key_format)
         self.cache.append(_bf(x.latent, device), _bf(x.keys, device))
-        self.key8 = Key8Index(_lib, _bf(x.keys, device), cfg.cap, B, cfg.Q, cfg.K, cfg.top_groups, device)
+        self.key8 = (Key8Index(_lib, _bf(x.keys, device), cfg.cap, B, cfg.Q, cfg.K, cfg.top_groups, device)
+                     if key_format == "bf16" else None)
         self.swa_len = torch.from_numpy(x.swa_len).to(device)
         self.layers = []
         for L in layers:
@@ -132,9 +137,7 @@ class DecodeWorkload:
         self.stream = torch.cuda.current_stream()
 
     def append(self):
-        self._lib.append_fp4(self.new_lat, self.start, self.cache.records, idx_key=self.new_key,
-                             key_cache=self.cache.keys, group_sum=self.cache.group_sum,
-                             stream=self.stream)
+        self.cache.write(self.new_lat, self.new_key, self.start, stream=self.stream)
 
     def step(self):
         self.append()
@@ -159,8 +162,8 @@ class DecodeWorkload:
                              len(self.layers)),
             # the two branches as separate calls (not part of the step; sparse_attn is the roofline unit)
             "sparse_attn": (self.sparse_attn_call, 0),
-            "index_topk_key8": (lambda: self.key8.call(L0["q_idx"], L0["w"], self.cache.n_entries, self.q_pos, s),
-                                0),
+            **({"index_topk_key8": (lambda: self.key8.call(L0["q_idx"], L0["w"], self.cache.n_entries,
+                                                            self.q_pos, s), 0)} if self.key8 else {}),
             "swa_merge": (lambda: lib.swa_merge(L0["q"], L0["swa"], self.swa_len, self.cfg.W, m.SCALE,
                                                 buf.o, buf.lse, buf.out, buf.lse_out, buf.ws_swa,
                                                 swa_pos0=self.swa_pos0, q_pos=self.q_pos, stream=s), 0),
@@ -182,7 +185,7 @@ class DecodeWorkload:
 class PrefillWorkload:
     """Chunked prefill: Q query tokens after ``prior`` cached entries, causal everywhere."""
 
-    def __init__(self, cfg, p, device="cuda"):
+    def __init__(self, cfg, p, device="cuda", key_format="bf16"):
         import torch
         from sparse_attention_fp4_csa2_amd import _lib, modes
         self.torch, self._lib, self.modes = torch, _lib, modes
@@ -190,9 +193,10 @@ class PrefillWorkload:
         N, prior = int(p["n_entries"][0]), int(p["prior"])
         Q = p["q"].shape[1]
         self.B, self.rows = 1, Q
-        self.cache = modes.LatentCache.empty(1, cfg.cap, device)
+        self.cache = modes.LatentCache.empty(1, cfg.cap, device, key_format=key_format)
         self.cache.append(_bf(p["latent"], device), _bf(p["keys"], device))
-        self.key8 = Key8Index(_lib, _bf(p["keys"], device), cfg.cap, 1, Q, cfg.K, 0, device)
+        self.key8 = Key8Index(_lib, _bf(p["keys"], device), cfg.cap, 1, Q, cfg.K, 0, device) \
+            if key_format == "bf16" else None
         self.buf = modes.LayerBuffers(1, Q, cfg.H, cfg.cap, cfg.K, cfg.W, device=device)
         self.q = _bf(p["q"], device)
         self.q_idx = _bf(p["q_idx"], device)
@@ -208,8 +212,7 @@ class PrefillWorkload:
         self.stream = torch.cuda.current_stream()
 
     def append(self):
-        self._lib.append_fp4(self.chunk_lat, self.start, self.cache.records, idx_key=self.chunk_key,
-                             key_cache=self.cache.keys, stream=self.stream)
+        self.cache.write(self.chunk_lat, self.chunk_key, self.start, stream=self.stream)
 
     def index(self):
         self.modes.index(self.buf, self.cache, self.q_idx, self.w, q_pos=self.q_pos, stream=self.stream)
@@ -239,8 +242,9 @@ class PrefillWorkload:
         return {"append": (self.append, 1), "index_topk": (self.index, 1),
                 "attend_layer": (self.attend_call, 1),
                 "sparse_attn": (self.sparse_attn_call, 0), "swa_merge": (self.swa_call, 0),
-                "index_topk_key8": (lambda: self.key8.call(self.q_idx, self.w, self.cache.n_entries, self.q_pos,
-                                                           self.stream), 0)}
+                **({"index_topk_key8": (lambda: self.key8.call(self.q_idx, self.w, self.cache.n_entries,
+                                                                self.q_pos, self.stream), 0)}
+                   if self.key8 else {})}
 
     def attended_entries(self):
         """Visible entries of the selected blocks summed over rows (causal masking counted)."""
@@ -261,20 +265,20 @@ def _bf(a, device):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
 
 
-def make_workload(name, device="cuda"):
+def make_workload(name, device="cuda", key_format="bf16"):
     """(cfg, host inputs, workload) for a named config, as bench.py times it."""
     from synth import CONFIGS, decode_inputs, layers_inputs, prefill_inputs, specdec_inputs
     from synth.gen import LayerInputs
     cfg = CONFIGS[name]
     if name == "prefill":
         p = prefill_inputs(cfg)
-        return cfg, p, PrefillWorkload(cfg, p, device)
+        return cfg, p, PrefillWorkload(cfg, p, device, key_format)
     if len(cfg.layers) > 1:
         x, layers = layers_inputs(cfg)
     else:
         x = specdec_inputs(cfg) if cfg.Q > 1 else decode_inputs(cfg)
         layers = [LayerInputs("F", x.q, x.q_idx, x.w, x.swa, x.planted)]
-    return cfg, (x, layers), DecodeWorkload(cfg, x, layers, device)
+    return cfg, (x, layers), DecodeWorkload(cfg, x, layers, device, key_format)
 
 
 # ---------------------------------------------------------------------------
@@ -292,7 +296,7 @@ def main():
     from sparse_attention_fp4_csa2_amd import _lib
     _lib.load()
     t0 = time.time()
-    cfg, host_in, wl = make_workload(args.config)
+    cfg, host_in, wl = make_workload(args.config, key_format=args.index_keys)
     gen_s = time.time() - t0
     stream = wl.stream
     torch.cuda.synchronize()
@@ -379,7 +383,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic (seeded N(0,1) bf16, planted relevant blocks)",
-        "config": workload_config(cfg, rows),
+        "config": workload_config(cfg, rows, args.index_keys),
         "fp4_kv_read_TBps": round(kv_tbps, 3),
         "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
         "launches_per_step": per_step,
@@ -400,13 +404,15 @@ def main():
         result["measured_peaks"] = peaks
         result["roofline"]["frac_of_measured_gemm"] = round(attn_tflops / peaks["bf16_gemm_TFLOPs"], 4)
     if not prefill:
-        idx_bytes = wl.B * cfg.N * 128 if not cfg.top_groups else \
-            wl.B * (cfg.cap // 512 * 256 + cfg.top_groups * 512 * 128)
+        kb = 128 if args.index_keys == "bf16" else 66     # key bytes: bf16, or MXFP8 codes + scales
+        idx_bytes = wl.B * cfg.N * kb if not cfg.top_groups else \
+            wl.B * (cfg.cap // 512 * 256 + cfg.top_groups * 512 * kb)
         result["indexer_GBps"] = round(idx_bytes / (breakdown["index_topk"] * 1e-3) / 1e9, 1)
-        # the same call on the MXFP8 key cache: 64 code bytes + 2 scale bytes per key
-        idx8_bytes = wl.B * cfg.N * 66 if not cfg.top_groups else \
-            wl.B * (cfg.cap // 512 * 256 + cfg.top_groups * 512 * 66)
-        result["indexer_key8_GBps"] = round(idx8_bytes / (breakdown["index_topk_key8"] * 1e-3) / 1e9, 1)
+        if "index_topk_key8" in breakdown:
+            # the same call on the MXFP8 key cache: 64 code bytes + 2 scale bytes per key
+            idx8_bytes = wl.B * cfg.N * 66 if not cfg.top_groups else \
+                wl.B * (cfg.cap // 512 * 256 + cfg.top_groups * 512 * 66)
+            result["indexer_key8_GBps"] = round(idx8_bytes / (breakdown["index_topk_key8"] * 1e-3) / 1e9, 1)
     if len(cfg.layers) > 1:
         result["reuse_saving_ms"] = round(breakdown["index_topk"] * cfg.layers.count("U"), 4)
 
@@ -457,7 +463,7 @@ def kernels_per_layer(cfg):
     return {m: (index + 2 if m in ("F", "R") else 2) for m in modes}
 
 
-def workload_config(cfg, rows):
+def workload_config(cfg, rows, index_keys="bf16"):
     if cfg.name == "prefill":
         desc = (f"prefill: {cfg.Q} query tokens after {cfg.prior} cached entries (+{cfg.Q // 2} "
                 f"appended), H {cfg.H}, indexer {cfg.Hi}x64, top-K {cfg.K} per row, window {cfg.W}, causal")
@@ -469,6 +475,8 @@ def workload_config(cfg, rows):
                 + (f", layers {'/'.join(cfg.layers)}" if len(cfg.layers) > 1 else "")
                 + (f", {cfg.Q} rows per sequence (1 + {cfg.Q - 1} drafts verified together)"
                    if cfg.Q > 1 else ""))
+    if index_keys != "bf16":
+        desc += f", {index_keys.upper()} indexer keys"
     return {"workload": desc, "global_batch": rows, "seq_len": 2 * cfg.N, "parallelism": "single GPU"}
 
 

@@ -113,15 +113,17 @@ size_t csa2_index_topk_ws(int B, int Q, int cap, int top_groups);
  * [B][n_new][64]) into entries start_entry[b] .. of key8 u8 [B][cap][64]
  * (byte d = dim d; 16-B aligned) and key8_scale u8 [B][cap][2] (byte g for
  * dims 32g..32g+31; 4-B aligned), and adds the dequantised keys to group_sum
- * fp32 [B][cap/512][64] when it is not NULL (cap % 512 == 0).  Pair it with
- * csa2_append_fp4(..., idx_key = NULL, key_cache = NULL, group_sum = NULL)
- * for the latent.  Entries at or beyond cap are skipped.
+ * fp32 [B][cap/512][64] when it is not NULL (cap % 512 == 0).  With latent
+ * and cache (both or neither) it also writes the latent's MXFP4 records as
+ * csa2_append_fp4 does, in the same launch.  Entries at or beyond cap are
+ * skipped.
  *
  * csa2_index_topk_key8: csa2_index_topk on such a cache (the scores use the
  * dequantised keys, exact in bf16, against the bf16 query); same outputs,
  * workspace (csa2_index_topk_ws) and errors. */
-int csa2_append_key8(const uint16_t* idx_key, const int32_t* start_entry, int B, int n_new, int cap,
-                     uint8_t* key8, uint8_t* key8_scale, float* group_sum, void* stream);
+int csa2_append_key8(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry, int B,
+                     int n_new, int cap, uint8_t* cache, uint8_t* key8, uint8_t* key8_scale, float* group_sum,
+                     void* stream);
 int csa2_index_topk_key8(const uint16_t* q_idx, const float* w, const uint8_t* key8,
                          const uint8_t* key8_scale, const float* group_sum, const int32_t* n_entries,
                          const int32_t* q_pos, int B, int Q, int Hi, int cap, int top_k, int top_groups,

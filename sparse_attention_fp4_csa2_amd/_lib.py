@@ -26,7 +26,7 @@ _SIGS = {
     "csa2_append_fp4": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
     "csa2_index_topk": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "csa2_index_topk_ws": (_SZ, [_I, _I, _I, _I]),
-    "csa2_append_key8": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _P]),
+    "csa2_append_key8": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
     "csa2_index_topk_key8": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "csa2_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "csa2_sparse_attn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]),
@@ -135,13 +135,15 @@ def index_topk(q_idx, w, key_cache, n_entries, top_k, idx, count, ws, group_sum=
     _check(rc, "csa2_index_topk")
 
 
-def append_key8(idx_key, start_entry, key8, key8_scale, group_sum=None, stream=None):
-    """csa2_append_key8: keys bf16 [B][n_new][64] -> key8 u8 [B][cap][64], key8_scale u8 [B][cap][2]."""
+def append_key8(idx_key, start_entry, key8, key8_scale, group_sum=None, latent=None, cache=None, stream=None):
+    """csa2_append_key8: keys bf16 [B][n_new][64] -> key8 u8 [B][cap][64], key8_scale u8 [B][cap][2]
+    (and, with latent bf16 [B][n_new][512] and cache u8 [B][cap/8][2176], the latent's records)."""
     lib = load()
     B, n_new = idx_key.shape[0], idx_key.shape[1]
     cap = key8.shape[1]
-    rc = lib.csa2_append_key8(_bf16_ptr(idx_key, "idx_key"), _ptr(start_entry, torch.int32, "start_entry"),
-                              B, n_new, cap, _ptr(key8, torch.uint8, "key8"),
+    rc = lib.csa2_append_key8(_bf16_ptr(latent, "latent"), _bf16_ptr(idx_key, "idx_key"),
+                              _ptr(start_entry, torch.int32, "start_entry"), B, n_new, cap,
+                              _ptr(cache, torch.uint8, "cache"), _ptr(key8, torch.uint8, "key8"),
                               _ptr(key8_scale, torch.uint8, "key8_scale"),
                               _ptr(group_sum, torch.float32, "group_sum"), _stream(stream))
     _check(rc, "csa2_append_key8")

@@ -189,18 +189,21 @@ int csa2_index_topk_key8(const uint16_t* q_idx, const float* w, const uint8_t* k
                     count, ws, ws_bytes, stream);
 }
 
-int csa2_append_key8(const uint16_t* idx_key, const int32_t* start_entry, int B, int n_new, int cap,
-                     uint8_t* key8, uint8_t* key8_scale, float* group_sum, void* stream) {
+int csa2_append_key8(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry, int B,
+                     int n_new, int cap, uint8_t* cache, uint8_t* key8, uint8_t* key8_scale, float* group_sum,
+                     void* stream) {
   if (!idx_key || !start_entry || !key8 || !key8_scale) return CSA2_ERR_INVALID_ARG;
+  if ((latent == nullptr) != (cache == nullptr)) return CSA2_ERR_INVALID_ARG;
   if (B <= 0 || n_new < 0 || cap <= 0 || cap % CSA2_BLOCK != 0) return CSA2_ERR_INVALID_ARG;
   if (!aligned(key8, 16) || !aligned(key8_scale, 4)) return CSA2_ERR_INVALID_ARG;
+  if (latent && (!aligned(latent, 16) || !aligned(cache, 16))) return CSA2_ERR_INVALID_ARG;
   if (group_sum) {
     if (cap % 512 != 0) return CSA2_ERR_UNSUPPORTED;
     if (!aligned(group_sum, 16)) return CSA2_ERR_INVALID_ARG;
   }
   if (n_new == 0) return CSA2_OK;
-  return launch_status(launch_append_key8(idx_key, start_entry, B, n_new, cap, key8, key8_scale, group_sum,
-                                          as_stream(stream)));
+  return launch_status(launch_append_key8(latent, idx_key, start_entry, B, n_new, cap, cache, key8, key8_scale,
+                                          group_sum, as_stream(stream)));
 }
 
 int csa2_topk(const float* scores, int rows, int n, int k, int32_t* idx, int32_t* count,

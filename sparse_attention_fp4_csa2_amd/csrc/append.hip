@@ -43,16 +43,65 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t mag, int sb) {
   return c;
 }
 
+// ---- MXFP8 indexer keys -------------------------------------------------
+// E4M3 magnitude code (0..126) of |x| / 2^(sb-127), round to nearest, halfway
+// to the even code, saturating at 448 (code 126).  mag = bf16 magnitude bits.
+// |x| / X = sig * 2^p exactly; its E4M3 binade is e = floor(log2) + 7 (codes
+// 8(e-1) .. 8(e-1)+15 step 2^(e-10) for e >= 1; below 2^-6 the step is 2^-9),
+// so n = round(|x| / X / step) and code = 8 (max(e, 1) - 1) + n (n = 16 carries
+// into the next binade).
+__device__ __forceinline__ uint32_t e4m3_code(uint32_t mag, int sb) {
+  const uint32_t ef = mag >> 7;
+  const uint32_t sig = ef ? (0x80u | (mag & 0x7Fu)) : (mag & 0x7Fu);
+  if (sig == 0) return 0;
+  const int p = (ef ? (int)ef : 1) - 7 - sb;           // |x| / X = sig * 2^p
+  const int lg = 31 - __builtin_clz(sig);               // floor(log2 sig)
+  const int e = lg + p + 7;
+  const int qe = (e > 1 ? e : 1) - 10;                  // log2 of the grid step
+  const int s = qe - p;                                 // n = sig / 2^s
+  uint32_t n;
+  if (s <= 0) {
+    n = sig << (-s);
+  } else if (s >= 10) {
+    n = 0;                                              // below half the smallest step
+  } else {
+    const uint32_t n0 = sig >> s, rem = sig & ((1u << s) - 1u), half = 1u << (s - 1);
+    n = n0 + ((rem > half || (rem == half && (n0 & 1u))) ? 1u : 0u);
+  }
+  const uint32_t code = 8u * (uint32_t)((e > 1 ? e : 1) - 1) + n;
+  return code > 126u ? 126u : code;
+}
+
+// MXFP8 key of new entry i at cache entry j, by one wave: lane d holds dim d;
+// the 32 lanes of a scale group agree on the group's largest magnitude.
+__device__ __forceinline__ void write_key8(const uint16_t* __restrict__ idx_key, int b, int i, int n_new,
+                                           long long j, int cap, int lane, uint8_t* __restrict__ key8,
+                                           uint8_t* __restrict__ key8_scale) {
+  const uint32_t v = idx_key[((size_t)b * n_new + i) * DI + lane];
+  uint32_t amax = v & 0x7FFFu;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
+  const int sb = amax ? min(max(floor_log2_bf16(amax) - 8 + 127, 0), 254) : 0;
+  const uint32_t code = ((v >> 15) << 7) | e4m3_code(v & 0x7FFFu, sb);
+  key8[((size_t)b * cap + (size_t)j) * DI + lane] = (uint8_t)code;
+  if ((lane & 31) == 0) key8_scale[((size_t)b * cap + (size_t)j) * 2 + (lane >> 5)] = (uint8_t)sb;
+}
+
+// One wave per new entry: the latent's MXFP4 record bytes (latent may be
+// null: keys only), and its indexer key as bf16 (key_cache) or MXFP8 (key8).
 __global__ __launch_bounds__(256) void append_fp4_kernel(
     const uint16_t* __restrict__ latent, const uint16_t* __restrict__ idx_key,
     const int32_t* __restrict__ start_entry, int n_new, int cap,
-    uint8_t* __restrict__ cache, uint16_t* __restrict__ key_cache) {
+    uint8_t* __restrict__ cache, uint16_t* __restrict__ key_cache,
+    uint8_t* __restrict__ key8, uint8_t* __restrict__ key8_scale) {
   const int b = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave;          // new entry index
   if (i >= n_new) return;
   const long long j = (long long)start_entry[b] + i;   // cache entry position
   if (j < 0 || j >= cap) return;
+  if (key8 != nullptr) write_key8(idx_key, b, i, n_new, j, cap, lane, key8, key8_scale);
+  if (latent == nullptr) return;
 
   const uint16_t* src = latent + ((size_t)b * n_new + i) * D + lane * 8;
   uint4 raw = *reinterpret_cast<const uint4*>(src);
@@ -107,56 +156,6 @@ __global__ __launch_bounds__(64) void group_sum_kernel(
   group_sum[((size_t)b * (cap / GROUP_ENTRIES) + (size_t)g) * DI + d] += acc;
 }
 
-// ---- MXFP8 indexer keys -------------------------------------------------
-// E4M3 magnitude code (0..126) of |x| / 2^(sb-127), round to nearest, halfway
-// to the even code, saturating at 448 (code 126).  mag = bf16 magnitude bits.
-// |x| / X = sig * 2^p exactly; its E4M3 binade is e = floor(log2) + 7 (codes
-// 8(e-1) .. 8(e-1)+15 step 2^(e-10) for e >= 1; below 2^-6 the step is 2^-9),
-// so n = round(|x| / X / step) and code = 8 (max(e, 1) - 1) + n (n = 16 carries
-// into the next binade).
-__device__ __forceinline__ uint32_t e4m3_code(uint32_t mag, int sb) {
-  const uint32_t ef = mag >> 7;
-  const uint32_t sig = ef ? (0x80u | (mag & 0x7Fu)) : (mag & 0x7Fu);
-  if (sig == 0) return 0;
-  const int p = (ef ? (int)ef : 1) - 7 - sb;           // |x| / X = sig * 2^p
-  const int lg = 31 - __builtin_clz(sig);               // floor(log2 sig)
-  const int e = lg + p + 7;
-  const int qe = (e > 1 ? e : 1) - 10;                  // log2 of the grid step
-  const int s = qe - p;                                 // n = sig / 2^s
-  uint32_t n;
-  if (s <= 0) {
-    n = sig << (-s);
-  } else if (s >= 10) {
-    n = 0;                                              // below half the smallest step
-  } else {
-    const uint32_t n0 = sig >> s, rem = sig & ((1u << s) - 1u), half = 1u << (s - 1);
-    n = n0 + ((rem > half || (rem == half && (n0 & 1u))) ? 1u : 0u);
-  }
-  const uint32_t code = 8u * (uint32_t)((e > 1 ? e : 1) - 1) + n;
-  return code > 126u ? 126u : code;
-}
-
-// One wave per new key: lane d holds dim d; the 32 lanes of a scale group
-// agree on the group's largest magnitude.
-__global__ __launch_bounds__(256) void append_key8_kernel(
-    const uint16_t* __restrict__ idx_key, const int32_t* __restrict__ start_entry, int n_new, int cap,
-    uint8_t* __restrict__ key8, uint8_t* __restrict__ key8_scale) {
-  const int b = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + wave;
-  if (i >= n_new) return;
-  const long long j = (long long)start_entry[b] + i;
-  if (j < 0 || j >= cap) return;
-  const uint32_t v = idx_key[((size_t)b * n_new + i) * DI + lane];
-  uint32_t amax = v & 0x7FFFu;
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
-  const int sb = amax ? min(max(floor_log2_bf16(amax) - 8 + 127, 0), 254) : 0;
-  const uint32_t code = ((v >> 15) << 7) | e4m3_code(v & 0x7FFFu, sb);
-  key8[((size_t)b * cap + (size_t)j) * DI + lane] = (uint8_t)code;
-  if ((lane & 31) == 0) key8_scale[((size_t)b * cap + (size_t)j) * 2 + (lane >> 5)] = (uint8_t)sb;
-}
-
 // E4M3 code -> value (finite codes; exact in fp32 with the power-of-two scale)
 __device__ __forceinline__ float e4m3_value(uint32_t c, int sb) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
@@ -185,10 +184,12 @@ __global__ __launch_bounds__(64) void group_sum_key8_kernel(
   group_sum[((size_t)b * (cap / GROUP_ENTRIES) + (size_t)g) * DI + d] += acc;
 }
 
-int launch_append_key8(const uint16_t* idx_key, const int32_t* start_entry, int B, int n_new, int cap,
-                       uint8_t* key8, uint8_t* key8_scale, float* group_sum, hipStream_t stream) {
+int launch_append_key8(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry, int B,
+                       int n_new, int cap, uint8_t* cache, uint8_t* key8, uint8_t* key8_scale, float* group_sum,
+                       hipStream_t stream) {
   dim3 grid((n_new + 3) / 4, B);
-  append_key8_kernel<<<grid, 256, 0, stream>>>(idx_key, start_entry, n_new, cap, key8, key8_scale);
+  append_fp4_kernel<<<grid, 256, 0, stream>>>(latent, idx_key, start_entry, n_new, cap, cache, nullptr, key8,
+                                              key8_scale);
   if (group_sum != nullptr) {
     dim3 g2((n_new + GROUP_ENTRIES - 1) / GROUP_ENTRIES + 1, B);
     group_sum_key8_kernel<<<g2, 64, 0, stream>>>(key8, key8_scale, start_entry, n_new, cap, group_sum);
@@ -201,7 +202,7 @@ int launch_append(const uint16_t* latent, const uint16_t* idx_key, const int32_t
                   float* group_sum, hipStream_t stream) {
   dim3 grid((n_new + 3) / 4, B);
   append_fp4_kernel<<<grid, 256, 0, stream>>>(latent, idx_key, start_entry, n_new, cap, cache,
-                                              key_cache);
+                                              key_cache, nullptr, nullptr);
   if (group_sum != nullptr) {
     dim3 g2((n_new + GROUP_ENTRIES - 1) / GROUP_ENTRIES + 1, B);
     group_sum_kernel<<<g2, 64, 0, stream>>>(idx_key, start_entry, n_new, cap, group_sum);

@@ -12,9 +12,11 @@ int launch_append(const uint16_t* latent, const uint16_t* idx_key, const int32_t
                   float* group_sum, hipStream_t stream);
 
 // MXFP8 indexer keys (append.hip): E4M3 codes [B][cap][64] + E8M0 scales
-// [B][cap][2]; group sums (optional) of the dequantised keys
-int launch_append_key8(const uint16_t* idx_key, const int32_t* start_entry, int B, int n_new, int cap,
-                       uint8_t* key8, uint8_t* key8_scale, float* group_sum, hipStream_t stream);
+// [B][cap][2], with the latent's records in the same launch when latent is
+// not null; group sums (optional) of the dequantised keys
+int launch_append_key8(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry, int B,
+                       int n_new, int cap, uint8_t* cache, uint8_t* key8, uint8_t* key8_scale, float* group_sum,
+                       hipStream_t stream);
 
 // Indexer keys: bf16 [B][cap][64] (bf16 != nullptr) or MXFP8 (codes, scales).
 struct KeyCache {

@@ -22,29 +22,46 @@ SCALE = 1.0 / math.sqrt(512.0)
 
 @dataclass
 class LatentCache:
-    """Device state shared by the layers: MXFP4 records, indexer keys, group sums."""
+    """Device state shared by the layers: MXFP4 records, indexer keys, group sums.
+
+    The indexer keys are bf16 (``keys``) or, in the lower-precision key cache,
+    MXFP8 (``key8`` E4M3 codes + ``key8_scale`` E8M0 scales; ``keys`` is None).
+    """
     records: torch.Tensor     # u8 [B][cap/8][2176]
-    keys: torch.Tensor        # bf16 [B][cap][64]
+    keys: torch.Tensor        # bf16 [B][cap][64], or None
     group_sum: torch.Tensor   # fp32 [B][cap/512][64] or None
     n_entries: torch.Tensor   # int32 [B]
+    key8: torch.Tensor = None        # u8 [B][cap][64]
+    key8_scale: torch.Tensor = None  # u8 [B][cap][2]
 
     @property
     def cap(self):
-        return self.keys.shape[1]
+        return self.records.shape[1] * _lib.BLOCK
 
     @staticmethod
-    def empty(B, cap, device="cuda", with_groups=False):
+    def empty(B, cap, device="cuda", with_groups=False, key_format="bf16"):
+        if key_format not in ("bf16", "mxfp8"):
+            raise ValueError(f"unknown key format {key_format!r}")
         rec = torch.zeros(B, cap // 8, _lib.RECORD_BYTES, dtype=torch.uint8, device=device)
-        keys = torch.zeros(B, cap, 64, dtype=torch.bfloat16, device=device)
         gs = torch.zeros(B, cap // 512, 64, dtype=torch.float32, device=device) if with_groups else None
         n = torch.zeros(B, dtype=torch.int32, device=device)
-        return LatentCache(rec, keys, gs, n)
+        if key_format == "bf16":
+            return LatentCache(rec, torch.zeros(B, cap, 64, dtype=torch.bfloat16, device=device), gs, n)
+        return LatentCache(rec, None, gs, n, torch.zeros(B, cap, 64, dtype=torch.uint8, device=device),
+                           torch.zeros(B, cap, 2, dtype=torch.uint8, device=device))
+
+    def write(self, latent, keys, start, stream=None):
+        """Write n_new entries per sequence at entries start[b] .. (start int32 [B] on the device)."""
+        if self.key8 is None:
+            _lib.append_fp4(latent, start, self.records, idx_key=keys, key_cache=self.keys,
+                            group_sum=self.group_sum, stream=stream)
+        else:
+            _lib.append_key8(keys, start, self.key8, self.key8_scale, group_sum=self.group_sum, latent=latent,
+                             cache=self.records, stream=stream)
 
     def append(self, latent, keys, stream=None):
         """Append n_new entries per sequence at each sequence's current end."""
-        start = self.n_entries.clone()
-        _lib.append_fp4(latent, start, self.records, idx_key=keys, key_cache=self.keys,
-                        group_sum=self.group_sum, stream=stream)
+        self.write(latent, keys, self.n_entries.clone(), stream=stream)
         self.n_entries += latent.shape[1]
 
 
@@ -73,9 +90,14 @@ def _ws(nbytes, dev):
 
 
 def index(buf, cache, q_idx, w, q_pos=None, stream=None):
-    _lib.index_topk(q_idx, w, cache.keys, cache.n_entries, buf.top_k, buf.idx, buf.count,
-                    buf.ws_index, group_sum=cache.group_sum if buf.top_groups else None,
-                    q_pos=q_pos, top_groups=buf.top_groups, stream=stream)
+    gs = cache.group_sum if buf.top_groups else None
+    if cache.key8 is None:
+        _lib.index_topk(q_idx, w, cache.keys, cache.n_entries, buf.top_k, buf.idx, buf.count,
+                        buf.ws_index, group_sum=gs, q_pos=q_pos, top_groups=buf.top_groups, stream=stream)
+    else:
+        _lib.index_topk_key8(q_idx, w, cache.key8, cache.key8_scale, cache.n_entries, buf.top_k, buf.idx,
+                             buf.count, buf.ws_index, group_sum=gs, q_pos=q_pos, top_groups=buf.top_groups,
+                             stream=stream)
 
 
 def attend(buf, cache, q, swa, swa_len, idx=None, count=None, swa_pos0=None, q_pos=None,

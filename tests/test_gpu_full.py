@@ -17,17 +17,17 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import indexer, modes as om, mxfp4, topk
+from oracle import indexer, modes as om, mxfp4, mxfp8, topk
 from tests.gpu_util import assert_close_rms, assert_lse_close, host
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 GAP = 1e-2
 
 
-def _workload(name):
+def _workload(name, key_format="bf16"):
     import bench
-    print(f"[full] building {name}", flush=True)
-    cfg, host_in, wl = bench.make_workload(name)
+    print(f"[full] building {name} ({key_format} indexer keys)", flush=True)
+    cfg, host_in, wl = bench.make_workload(name, key_format=key_format)
     wl.step()
     wl.step()
     torch.cuda.synchronize()
@@ -69,8 +69,11 @@ def _check_selection(got_idx, got_cnt, scores, k, what, cand_mask=None):
     return False
 
 
-def _decode_checks(cfg, x, layers, wl, rows):
-    """rows: sequences to check; every query row of each (cfg.Q per sequence)."""
+def _decode_checks(cfg, x, layers, wl, rows, keys=None):
+    """rows: sequences to check; every query row of each (cfg.Q per sequence).
+
+    keys: the indexer keys the oracle scores (default: the bf16 keys)."""
+    keys = x.keys if keys is None else keys
     nb = cfg.cap // 8
     N = cfg.N
     Q = cfg.Q
@@ -85,11 +88,11 @@ def _decode_checks(cfg, x, layers, wl, rows):
         if L.mode in ("F", "R"):
             for b in range(x.latent.shape[0]):
                 for r in range(Q):
-                    s = indexer.block_scores(L.q_idx[b, r], L.w[b, r], x.keys[b], N, q_pos=qpos(b, r),
+                    s = indexer.block_scores(L.q_idx[b, r], L.w[b, r], keys[b], N, q_pos=qpos(b, r),
                                              n_blocks=nb)
                     mask = None
                     if cfg.top_groups:
-                        gs = indexer.group_scores(L.q_idx[b, r], L.w[b, r], x.keys[b], N, n_groups=nb // 64)
+                        gs = indexer.group_scores(L.q_idx[b, r], L.w[b, r], keys[b], N, n_groups=nb // 64)
                         assert topk.gap_at_rank(gs, cfg.top_groups) >= GAP, "generator gap at the group rank"
                         gsel, gc = topk.select(gs, cfg.top_groups)
                         mask = np.zeros(nb, dtype=bool)
@@ -132,6 +135,16 @@ def _decode_checks(cfg, x, layers, wl, rows):
 def test_decode64k_full_size():
     cfg, (x, layers), wl = _workload("decode64k")
     _decode_checks(cfg, x, layers, wl, rows=list(range(cfg.B)))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["decode64k", "decode1m"])
+def test_mxfp8_key_cache_full_size(name):
+    # the whole step on the MXFP8 indexer key cache (flat, and two-level with
+    # the group sums of the dequantised keys); the oracle scores the keys
+    # through its own MXFP8 encoding
+    cfg, (x, layers), wl = _workload(name, key_format="mxfp8")
+    _decode_checks(cfg, x, layers, wl, rows=list(range(cfg.B)), keys=mxfp8.quantize_dequantize(x.keys))
 
 
 @pytest.mark.timeout(600)

@@ -87,6 +87,32 @@ def test_append_key8_special_keys_and_group_sums():
         assert np.allclose(got_g[b][fin], exp[fin], rtol=1e-5, atol=1e-3)
 
 
+def test_append_key8_with_latent_one_launch_bit_exact():
+    # latent records and MXFP8 keys written by one call: the records equal the
+    # oracle's MXFP4 encoding, the keys its MXFP8 encoding (ragged start, one
+    # sequence running past capacity)
+    from oracle import mxfp4
+    lib = _lib()
+    rng = rng_for(89)
+    B, cap, n = 2, 1024, 300
+    lat = normal_bf16(rng, (B, n, 512))
+    keys = normal_bf16(rng, (B, n, 64))
+    cache = torch.zeros(B, cap // 8, 2176, dtype=torch.uint8, device="cuda")
+    key8 = torch.zeros(B, cap, 64, dtype=torch.uint8, device="cuda")
+    ks = torch.zeros(B, cap, 2, dtype=torch.uint8, device="cuda")
+    starts = [5, cap - 100]
+    lib.append_key8(dev_bf16(keys), dev(np.array(starts, np.int32)), key8, ks, latent=dev_bf16(lat), cache=cache)
+    torch.cuda.synchronize()
+    for b in range(B):
+        m = min(n, cap - starts[b])
+        ref = np.zeros((cap // 8, 2176), dtype=np.uint8)
+        mxfp4.write_records(ref, lat[b, :m], starts[b])
+        assert np.array_equal(host(cache)[b], ref), b
+        codes, sb = mxfp8.encode_keys(keys[b, :m])
+        assert np.array_equal(host(key8)[b, starts[b]:starts[b] + m], codes), b
+        assert np.array_equal(host(ks)[b, starts[b]:starts[b] + m], sb), b
+
+
 def _index_key8(keys, q_idx, w, n_entries, cap, K, q_pos=None, top_groups=0):
     lib = _lib()
     B, Q = q_idx.shape[:2]
