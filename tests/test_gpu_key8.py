@@ -150,12 +150,13 @@ def _check_rows(got, cnt, sc, keys_f, q_idx, w, n_entries, cap, K, q_pos=None):
     return worst
 
 
-@pytest.mark.parametrize("Q", [1, 40, 150])
-def test_index_topk_key8_scores_and_selection(Q):
+@pytest.mark.parametrize("Q,Hi", [(1, 8), (40, 8), (150, 8), (1, 5), (40, 5)])
+def test_index_topk_key8_scores_and_selection(Q, Hi):
     # Q = 1: the per-row decode kernel; 40 and 150 causal rows: the multi-row
-    # MFMA kernel (a partly filled workgroup; two full ones and a ragged one)
-    rng = rng_for(90 + Q)
-    B, cap, K, Hi = 2, 4096 + 512, 64, 8
+    # MFMA kernel (a partly filled workgroup; two full ones and a ragged one);
+    # Hi = 5 leaves padded head rows in both
+    rng = rng_for(90 + Q + Hi)
+    B, cap, K = 2, 4096 + 512, 64
     keys = normal_bf16(rng, (B, cap, 64))
     # sequence 1: keys scaled far from 1 in two ranges (E8M0 bytes ~27 and ~187)
     kf = (keys[1].astype(np.uint32) << 16).view(np.float32)
@@ -174,7 +175,7 @@ def test_index_topk_key8_scores_and_selection(Q):
     assert np.array_equal(k8, codes) and np.array_equal(ks, sb)   # ... which the GPU's bytes match
     keys_f = mxfp8.decode_keys(codes, sb)
     worst = _check_rows(got, cnt, sc, keys_f, q_idx, w, ne, cap, K, q_pos)
-    print(f"[parity] MXFP8-key block scores (Q={Q}): max|err|/max|s| = {worst:.2e}")
+    print(f"[parity] MXFP8-key block scores (Q={Q}, Hi={Hi}): max|err|/max|s| = {worst:.2e}")
     assert worst < 1e-5
 
 
