@@ -64,6 +64,9 @@ def parse(argv=None):
                     help="indexer key cache: bf16 (the workload's definition) or the lower-precision "
                          "MXFP8 variant")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="untimed steps for this long (seconds) before the warm-up steps, so the GPU "
+                         "clocks reach their steady state (they ramp over the first ~30 ms of work)")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="reps of the cold timings (a 1 GiB write before each evicts L2 and the 256 MB "
                          "last-level cache); 0 skips them")
@@ -301,6 +304,12 @@ def main():
     stream = wl.stream
     torch.cuda.synchronize()
 
+    # settle: the same step, untimed, until the clocks have ramped up
+    t_settle = time.time()
+    while time.time() - t_settle < args.settle_s:
+        for _ in range(10):
+            wl.step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         wl.step()
     torch.cuda.synchronize()
