@@ -62,6 +62,10 @@ enum {
 };
 
 /* Append n_new entries per sequence to the latent cache (MXFP4 quantise + pack).
+ * Defined by: the global cache held in FP4 (news.promptgoblins.ai, Details,
+ * "FP4 KVCache precision"; thelatestinai.com, Abstract), one entry per merged
+ * pair of raw positions (paper-digest.app, Core Mechanics, "Compressed along
+ * three axes"); the FP4 format is this library's choice, OCP MXFP4.
  * Encoding per 32-value group: amax = max |x|; sb = clamp(floor(log2 amax) - 2
  * + 127, 0, 254) (amax = 0 -> 0); codes = |x| / 2^(sb-127) rounded to the E2M1
  * grid {0,.5,1,1.5,2,3,4,6} to nearest, halfway cases to the even code, above 6
@@ -72,14 +76,26 @@ enum {
  *   start_entry int32 [B] (device): entry position of each sequence's first
  *               new entry; entries at positions >= cap are dropped
  *   cache       u8 [B][cap/8][2176]; key_cache bf16 [B][cap][64] or NULL
- *   group_sum   fp32 [B][cap/512][64] or NULL: each new key is added to its
- *               512-entry group's sum (needs idx_key and cap % 512 == 0)
- * Bytes of records not covered by new entries are left untouched. */
+ *   group_sum   fp32 [B][cap/512][64] or NULL (needs idx_key and cap % 512 ==
+ *               0): every 512-entry group the call writes into is recomputed
+ *               as the sum of the keys its 512 key_cache slots hold after the
+ *               call (slots holding no entry must be zero, as in a
+ *               zero-initialised cache), so an overwritten entry counts once,
+ *               with its new key.  The sum is formed in fp64 and rounded once
+ *               to fp32: exact up to that rounding for keys of ordinary range.
+ * Bytes of records not covered by new entries are left untouched.  Errors:
+ * CSA2_ERR_INVALID_ARG for a null latent / start_entry / cache, bad sizes,
+ * 16-byte misalignment, or idx_key without key_cache (or the reverse). */
 int csa2_append_fp4(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry,
                     int B, int n_new, int cap, uint8_t* cache, uint16_t* key_cache,
                     float* group_sum, void* stream);
 
 /* Indexer + top-K block selection for B*Q query rows.
+ * Defined by: the sparse indexer that picks up to 2048 blocks of 8 entries per
+ * query, rescored per layer in Reindex mode, two-level ("hierarchical") to trim
+ * decoder indexing (observer.broadside.tech card, Key ideas, "CSA2 with three
+ * static layer modes").  The pages print no score formula; the one below is
+ * this library's reading.
  * Entry score e_j = sum_h w_h * max(0, q_h . k_j) (fp32 accumulation); block
  * score = max over the block's present (j < n_entries[b]) and visible entries;
  * a block with none is not a candidate.  Visibility: with q_pos, entry j is
@@ -112,8 +128,9 @@ size_t csa2_index_topk_ws(int B, int Q, int cap, int top_groups);
  * csa2_append_key8: quantises n_new new keys per sequence (bf16 idx_key
  * [B][n_new][64]) into entries start_entry[b] .. of key8 u8 [B][cap][64]
  * (byte d = dim d; 16-B aligned) and key8_scale u8 [B][cap][2] (byte g for
- * dims 32g..32g+31; 4-B aligned), and adds the dequantised keys to group_sum
- * fp32 [B][cap/512][64] when it is not NULL (cap % 512 == 0).  With latent
+ * dims 32g..32g+31; 4-B aligned), and, when group_sum fp32 [B][cap/512][64] is
+ * not NULL (cap % 512 == 0), recomputes every group it writes into as the sum
+ * of the dequantised keys its 512 slots hold, as csa2_append_fp4 does.  With latent
  * and cache (both or neither) it also writes the latent's MXFP4 records as
  * csa2_append_fp4 does, in the same launch.  Entries at or beyond cap are
  * skipped.
@@ -137,13 +154,20 @@ int csa2_topk(const float* scores, int rows, int n, int k, int32_t* idx, int32_t
               void* stream);
 
 /* Sparse multi-head attention over the selected blocks of the latent cache.
+ * Defined by: one 512-d latent per entry is the key and the value of every
+ * query head (paper-digest.app, Core Mechanics, "Compressed along three
+ * axes"), attended over the selected blocks only (observer.broadside.tech
+ * card, Key ideas, "CSA2 with three static layer modes").
  * For each row r = (b, q) and head h: z_j = scale * (q_h . V_j) over the
  * present, visible entries j of the blocks idx[r][0..count[r]); V_j = the
  * dequantised entry; o = softmax(z) V (fp32), lse = log sum exp z.  An empty
  * selection gives o = 0, lse = -inf.  q . K runs on the scaled FP4 x FP6 MFMA
  * (each 32-dim block of the query split into three E2M3 terms that carry it to
- * within 2^-11.7 of the block's largest value, fp32 accumulation); the
- * softmax weights are rounded to fp16 before the value product with V in fp16.
+ * within 2^-11.7 of the block's largest value, fp32 accumulation); a wave whose
+ * query blocks spread too far for that (fewer than half of a block's values
+ * within 2^4 of its largest) uses two exact E4M3 terms on FP4 x FP8 instead.
+ * The softmax weights are rounded to fp16 before the value product with V in
+ * fp16.
  *   q bf16 [B][Q][H][512]; cache as above; idx int32 [B][Q][top_k];
  *   count int32 [B][Q]; n_entries int32 [B]; q_pos int32 [B][Q] or NULL
  *   o fp32 [B][Q][H][512]; lse fp32 [B][Q][H] (natural log)
@@ -155,6 +179,12 @@ int csa2_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx
 size_t csa2_sparse_attn_ws(int B, int Q, int H, int top_k);
 
 /* Sliding-window branch and log-sum-exp merge with the sparse branch.
+ * Defined by: every layer keeps its own query and sliding-window KV
+ * (observer.broadside.tech card, Key ideas, "CSA2 with three static layer
+ * modes"; the window is named in the paper-digest.app Terminology); the merge
+ * is the log-sum-exp combination of the two branches.  Beyond the four-call
+ * outline, this call also takes swa_pos0 (raw position of slot 0, so causal
+ * rows can sit inside the window) and a workspace for its split-K partials.
  * Window slot i of sequence b holds raw position swa_pos0[b] + i (swa_pos0
  * NULL = 0), for i < swa_len[b] <= Lw.  The query at raw position t (q_pos, or
  * NULL = the newest held token) attends positions [t-W+1, t] that are held.

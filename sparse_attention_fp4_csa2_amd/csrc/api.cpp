@@ -26,7 +26,6 @@ inline int launch_status(int rc) { return rc == 0 ? CSA2_OK : CSA2_ERR_LAUNCH; }
 // Index/top-K workspace pieces.
 struct IndexWs {
   size_t scores;      // fp32 [rows][n_score]
-  size_t gscores;     // fp32 [rows][cap/512]
   size_t gsel;        // int32 [rows][top_groups]
   size_t gcount;      // int32 [rows]
   size_t total;
@@ -39,7 +38,6 @@ IndexWs index_ws_layout(int B, int Q, int cap, int top_groups) {
   size_t off = 0;
   l.scores = off; off += align_up(rows * n_score * sizeof(float));
   if (top_groups > 0) {
-    l.gscores = off; off += align_up(rows * (size_t)(cap / 512) * sizeof(float));
     l.gsel = off; off += align_up(rows * (size_t)top_groups * sizeof(int32_t));
     l.gcount = off; off += align_up(rows * sizeof(int32_t));
   }
@@ -126,7 +124,11 @@ size_t csa2_index_topk_ws(int B, int Q, int cap, int top_groups) {
   return index_ws_layout(B, Q, cap, top_groups).total;
 }
 
-static int index_topk(const uint16_t* q_idx, const float* w, const KeyCache& keys,
+}  // extern "C"
+
+// The selection behind csa2_index_topk(_key8) and the no-allocation variant:
+// argument checks, workspace carving, launches.
+int csa2::index_topk_run(const uint16_t* q_idx, const float* w, const KeyCache& keys,
                       const float* group_sum, const int32_t* n_entries, const int32_t* q_pos,
                       int B, int Q, int Hi, int cap, int top_k, int top_groups,
                       int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
@@ -155,17 +157,17 @@ static int index_topk(const uint16_t* q_idx, const float* w, const KeyCache& key
   const int G = cap / 512;
   if (top_groups > G) return CSA2_ERR_INVALID_ARG;
   if ((size_t)top_groups * CSA2_GROUP_BLOCKS > 65536) return CSA2_ERR_UNSUPPORTED;
-  float* gscores = reinterpret_cast<float*>(base + l.gscores);
   int32_t* gsel = reinterpret_cast<int32_t*>(base + l.gsel);
   int32_t* gcount = reinterpret_cast<int32_t*>(base + l.gcount);
-  int rc = launch_group_scores(q_idx, w, group_sum, n_entries, B, Q, Hi, cap, gscores, st);
-  if (!rc) rc = launch_topk(gscores, rows, G, top_groups, nullptr, 0, gsel, gcount, st);
+  int rc = launch_coarse_select(q_idx, w, group_sum, n_entries, B, Q, Hi, cap, top_groups, gsel, gcount, st);
   if (!rc) rc = launch_index_scores(q_idx, w, keys, n_entries, nullptr, B, Q, Hi, cap, gsel, top_groups,
                                     scores, st);
   if (!rc) rc = launch_topk(scores, rows, top_groups * CSA2_GROUP_BLOCKS, top_k, gsel, top_groups,
                             idx, count, st);
   return launch_status(rc);
 }
+
+extern "C" {
 
 int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* key_cache,
                     const float* group_sum, const int32_t* n_entries, const int32_t* q_pos,
@@ -174,8 +176,8 @@ int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* key_c
   if (!key_cache) return CSA2_ERR_INVALID_ARG;
   if (!aligned(key_cache, 16)) return CSA2_ERR_INVALID_ARG;
   const KeyCache keys{key_cache, nullptr, nullptr};
-  return index_topk(q_idx, w, keys, group_sum, n_entries, q_pos, B, Q, Hi, cap, top_k, top_groups, idx,
-                    count, ws, ws_bytes, stream);
+  return csa2::index_topk_run(q_idx, w, keys, group_sum, n_entries, q_pos, B, Q, Hi, cap, top_k, top_groups,
+                              idx, count, ws, ws_bytes, stream);
 }
 
 int csa2_index_topk_key8(const uint16_t* q_idx, const float* w, const uint8_t* key8,
@@ -185,8 +187,8 @@ int csa2_index_topk_key8(const uint16_t* q_idx, const float* w, const uint8_t* k
   if (!key8 || !key8_scale) return CSA2_ERR_INVALID_ARG;
   if (!aligned(key8, 16) || !aligned(key8_scale, 4)) return CSA2_ERR_INVALID_ARG;
   const KeyCache keys{nullptr, key8, key8_scale};
-  return index_topk(q_idx, w, keys, group_sum, n_entries, q_pos, B, Q, Hi, cap, top_k, top_groups, idx,
-                    count, ws, ws_bytes, stream);
+  return csa2::index_topk_run(q_idx, w, keys, group_sum, n_entries, q_pos, B, Q, Hi, cap, top_k, top_groups,
+                              idx, count, ws, ws_bytes, stream);
 }
 
 int csa2_append_key8(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry, int B,

@@ -1,5 +1,5 @@
 // Cache append: MXFP4 quantise + pack of new latent entries, indexer-key copy
-// (bf16, or MXFP8 in the lower-precision key cache), group-sum update.
+// (bf16, or MXFP8 in the lower-precision key cache), group-sum recompute.
 //
 // Storage of the global latent cache in FP4 follows the news.promptgoblins.ai
 // summary (Details, "FP4 KVCache precision") and the thelatestinai.com
@@ -137,25 +137,6 @@ __global__ __launch_bounds__(256) void append_fp4_kernel(
   }
 }
 
-// Group sums: one 64-thread block per (sequence, touched group); thread d adds
-// the new keys of that group to dimension d in entry order (deterministic).
-__global__ __launch_bounds__(64) void group_sum_kernel(
-    const uint16_t* __restrict__ idx_key, const int32_t* __restrict__ start_entry,
-    int n_new, int cap, float* __restrict__ group_sum) {
-  const int b = blockIdx.y;
-  const int d = threadIdx.x;
-  const long long s0 = start_entry[b];
-  const long long g0 = s0 / GROUP_ENTRIES;
-  const long long g = g0 + blockIdx.x;
-  const long long lo = max(s0, g * GROUP_ENTRIES);
-  const long long hi = min(min(s0 + n_new, (g + 1) * GROUP_ENTRIES), (long long)cap);
-  if (s0 < 0 || lo >= hi) return;
-  float acc = 0.f;
-  for (long long j = lo; j < hi; ++j)
-    acc += bf16_to_f32(idx_key[((size_t)b * n_new + (size_t)(j - s0)) * DI + d]);
-  group_sum[((size_t)b * (cap / GROUP_ENTRIES) + (size_t)g) * DI + d] += acc;
-}
-
 // E4M3 code -> value (finite codes; exact in fp32 with the power-of-two scale)
 __device__ __forceinline__ float e4m3_value(uint32_t c, int sb) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
@@ -163,25 +144,69 @@ __device__ __forceinline__ float e4m3_value(uint32_t c, int sb) {
   return ldexpf((c & 0x80u) ? -mag : mag, sb - 127);
 }
 
-// Group sums of the stored (dequantised) MXFP8 keys, as group_sum_kernel:
-// one 64-thread block per (sequence, touched group), entries in order.
-__global__ __launch_bounds__(64) void group_sum_key8_kernel(
-    const uint8_t* __restrict__ key8, const uint8_t* __restrict__ key8_scale,
-    const int32_t* __restrict__ start_entry, int n_new, int cap, float* __restrict__ group_sum) {
+// Group sums, recomputed after the append for every 512-entry group it
+// touched: the sum of the keys held in all 512 slots of the group (slots that
+// hold no entry are zero in a zero-initialised cache), read back from the key
+// cache, so an overwritten entry counts once with its new key.  One 256-thread
+// block per (sequence, touched group): thread t sums dims [8(t%8), +8) over the
+// slots t/8, t/8 + 32, ... in fp64, and the 32 partials meet in LDS in a fixed
+// order.  fp64 holds the sum of 512 bf16 (or E4M3 x 2^k) values exactly unless
+// they span more than ~40 binades, so the stored fp32 is the exact sum rounded
+// once, whatever the order.
+template <bool K8>
+__global__ __launch_bounds__(256) void group_sum_kernel(
+    const uint16_t* __restrict__ key_cache, const uint8_t* __restrict__ key8,
+    const uint8_t* __restrict__ key8_scale, const int32_t* __restrict__ start_entry, int n_new, int cap,
+    float* __restrict__ group_sum) {
+  __shared__ double part[32][DI + 1];
   const int b = blockIdx.y;
-  const int d = threadIdx.x;
+  const int t = threadIdx.x, c = t & 7, r = t >> 3;
   const long long s0 = start_entry[b];
-  const long long g0 = s0 / GROUP_ENTRIES;
-  const long long g = g0 + blockIdx.x;
-  const long long lo = max(s0, g * GROUP_ENTRIES);
-  const long long hi = min(min(s0 + n_new, (g + 1) * GROUP_ENTRIES), (long long)cap);
-  if (s0 < 0 || lo >= hi) return;
-  float acc = 0.f;
-  for (long long j = lo; j < hi; ++j) {
-    const size_t e = (size_t)b * cap + (size_t)j;
-    acc += e4m3_value(key8[e * DI + d], key8_scale[e * 2 + (d >> 5)]);
+  const long long first = max(s0, 0LL), last = min(s0 + n_new, (long long)cap);   // written [first, last)
+  if (first >= last) return;
+  const long long g = first / GROUP_ENTRIES + blockIdx.x;
+  if (g * GROUP_ENTRIES >= last) return;
+  double acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.0;
+  const size_t e0 = (size_t)b * cap + (size_t)g * GROUP_ENTRIES;
+  constexpr int PER = GROUP_ENTRIES / 32;      // slots per thread, all requested before any is summed
+  if constexpr (K8) {
+    uint2 cw[PER];
+    int sbv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const size_t e = e0 + (size_t)(r + 32 * i);
+      cw[i] = *reinterpret_cast<const uint2*>(key8 + e * DI + 8 * c);
+      sbv[i] = key8_scale[e * 2 + (c >> 2)];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t w2[2] = {cw[i].x, cw[i].y};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] += (double)e4m3_value((w2[k >> 2] >> (8 * (k & 3))) & 0xFFu, sbv[i]);
+    }
+  } else {
+    uint4 kw[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      kw[i] = *reinterpret_cast<const uint4*>(key_cache + (e0 + (size_t)(r + 32 * i)) * DI + 8 * c);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t w4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        acc[k] += (double)__uint_as_float((k & 1) ? (w4[k >> 1] & 0xFFFF0000u) : (w4[k >> 1] << 16));
+    }
   }
-  group_sum[((size_t)b * (cap / GROUP_ENTRIES) + (size_t)g) * DI + d] += acc;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) part[r][8 * c + k] = acc[k];
+  __syncthreads();
+  if (t < DI) {
+    double s = 0.0;
+    for (int i = 0; i < 32; ++i) s += part[i][t];
+    group_sum[((size_t)b * (cap / GROUP_ENTRIES) + (size_t)g) * DI + t] = (float)s;
+  }
 }
 
 int launch_append_key8(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry, int B,
@@ -192,7 +217,7 @@ int launch_append_key8(const uint16_t* latent, const uint16_t* idx_key, const in
                                               key8_scale);
   if (group_sum != nullptr) {
     dim3 g2((n_new + GROUP_ENTRIES - 1) / GROUP_ENTRIES + 1, B);
-    group_sum_key8_kernel<<<g2, 64, 0, stream>>>(key8, key8_scale, start_entry, n_new, cap, group_sum);
+    group_sum_kernel<true><<<g2, 256, 0, stream>>>(nullptr, key8, key8_scale, start_entry, n_new, cap, group_sum);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
@@ -205,7 +230,7 @@ int launch_append(const uint16_t* latent, const uint16_t* idx_key, const int32_t
                                               key_cache, nullptr, nullptr);
   if (group_sum != nullptr) {
     dim3 g2((n_new + GROUP_ENTRIES - 1) / GROUP_ENTRIES + 1, B);
-    group_sum_kernel<<<g2, 64, 0, stream>>>(idx_key, start_entry, n_new, cap, group_sum);
+    group_sum_kernel<false><<<g2, 256, 0, stream>>>(key_cache, nullptr, nullptr, start_entry, n_new, cap, group_sum);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

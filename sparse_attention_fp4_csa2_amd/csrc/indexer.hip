@@ -16,6 +16,7 @@
 // Keys stream once from HBM with 32-byte loads per lane.
 #include "device.h"
 #include "launch.h"
+#include "select.h"
 
 namespace csa2 {
 
@@ -282,46 +283,59 @@ __global__ __launch_bounds__(256) void index_rows_kernel(
   if (e < e_end) score(e, k0);
 }
 
-// Coarse scores: grid (groups / 32, rows); thread (group t/8, head t%8) forms
-// the dot product of the head's query with the group's mean key (fp32 sum /
-// count) and the 8 heads of a group meet by lane shuffles.
-constexpr int GROUPS_PER_WG = 32;
+// Two-level stage, coarse part, in one launch: one 1024-thread workgroup per
+// query row, thread g = group g.  Each thread requests its group's 64 summed
+// key dims at once (one round of memory latency for the whole row), takes the
+// mean (sum / present count), and forms sum_h w_h max(0, q_h . mean) with the
+// row's indexer query read from LDS (fp32, staged once); the scores meet in LDS
+// and the radix select of the top-K kernels keeps the best top_groups groups
+// (ascending ids, -1 padded, with their count).  G = cap / 512 <= 1024
+// (cap / 8 <= 65536).
+constexpr int COARSE_TPB = 1024;
 
-__global__ __launch_bounds__(256) void group_scores_kernel(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const float* __restrict__ group_sum, const int32_t* __restrict__ n_entries, int Q, int Hi,
-    int cap, float* __restrict__ gscores) {
-  const int row = blockIdx.y, b = row / Q;
+__global__ __launch_bounds__(COARSE_TPB) void coarse_select_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const float* __restrict__ group_sum,
+    const int32_t* __restrict__ n_entries, int Q, int Hi, int cap, int top_groups, int32_t* __restrict__ gsel,
+    int32_t* __restrict__ gcount) {
+  __shared__ float4 qs[MAX_HI][DI / 4];
+  __shared__ float ws[MAX_HI];
+  const int row = blockIdx.x, b = row / Q;
   const int G = cap / GROUP_ENTRIES;
   const int ne = min(n_entries[b], cap);
   const int t = threadIdx.x;
-  const int g = blockIdx.x * GROUPS_PER_WG + (t >> 3);
-  const int h0 = t & 7;
-  float s = 0.f;
+  const int g = t;
   const int cnt = g < G ? min(GROUP_ENTRIES, ne - g * GROUP_ENTRIES) : 0;
+  float4 m4[DI / 4];
   if (cnt > 0) {
     const float4* gs = reinterpret_cast<const float4*>(group_sum + ((size_t)b * G + g) * DI);
-    float4 m4[DI / 4];
 #pragma unroll
     for (int d4 = 0; d4 < DI / 4; ++d4) m4[d4] = gs[d4];
+  }
+  if (t < Hi * (DI / 4)) {
+    const int h = t / (DI / 4), d4 = t % (DI / 4);
+    const uint2 qq = *reinterpret_cast<const uint2*>(q_idx + ((size_t)row * Hi + h) * DI + 4 * d4);
+    qs[h][d4] = make_float4(__uint_as_float(qq.x << 16), __uint_as_float(qq.x & 0xFFFF0000u),
+                            __uint_as_float(qq.y << 16), __uint_as_float(qq.y & 0xFFFF0000u));
+  }
+  if (t < Hi) ws[t] = w[(size_t)row * Hi + t];
+  __syncthreads();
+  float s = -__builtin_inff();
+  if (cnt > 0) {
     const float inv = 1.f / (float)cnt;
-    // heads h0, h0 + 8 (Hi <= 16)
-    for (int h = h0; h < Hi; h += 8) {
-      const uint16_t* qh = q_idx + ((size_t)row * Hi + h) * DI;
+    s = 0.f;
+    for (int h = 0; h < Hi; ++h) {
       float dot = 0.f;
 #pragma unroll
       for (int d4 = 0; d4 < DI / 4; ++d4) {
-        const uint2 qq = *reinterpret_cast<const uint2*>(qh + 4 * d4);
-        dot += __uint_as_float(qq.x << 16) * m4[d4].x + __uint_as_float(qq.x & 0xFFFF0000u) * m4[d4].y +
-               __uint_as_float(qq.y << 16) * m4[d4].z + __uint_as_float(qq.y & 0xFFFF0000u) * m4[d4].w;
+        const float4 q4 = qs[h][d4];
+        dot += q4.x * m4[d4].x + q4.y * m4[d4].y + q4.z * m4[d4].z + q4.w * m4[d4].w;
       }
-      s += w[(size_t)row * Hi + h] * fmaxf(dot * inv, 0.f);
+      s += ws[h] * fmaxf(dot * inv, 0.f);
     }
   }
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
-  s += __shfl_xor(s, 4, 64);
-  if (h0 == 0 && g < G) gscores[(size_t)row * G + g] = cnt > 0 ? s : -__builtin_inff();
+  uint32_t key[1] = {g < G ? score_key(s) : 0u};
+  sel::select_core<COARSE_TPB, 1, false>(key, G, top_groups, nullptr, 0, row, gsel + (size_t)row * top_groups,
+                                         gcount + row);
 }
 
 template <bool K8>
@@ -360,12 +374,12 @@ int launch_index_scores(const uint16_t* q_idx, const float* w, const KeyCache& k
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int launch_group_scores(const uint16_t* q_idx, const float* w, const float* group_sum,
-                        const int32_t* n_entries, int B, int Q, int Hi, int cap, float* gscores,
-                        hipStream_t stream) {
-  const int G = cap / GROUP_ENTRIES;
-  dim3 grid((G + GROUPS_PER_WG - 1) / GROUPS_PER_WG, B * Q);
-  group_scores_kernel<<<grid, 256, 0, stream>>>(q_idx, w, group_sum, n_entries, Q, Hi, cap, gscores);
+int launch_coarse_select(const uint16_t* q_idx, const float* w, const float* group_sum,
+                         const int32_t* n_entries, int B, int Q, int Hi, int cap, int top_groups, int32_t* gsel,
+                         int32_t* gcount, hipStream_t stream) {
+  if (cap / GROUP_ENTRIES > COARSE_TPB) return -4;
+  coarse_select_kernel<<<B * Q, COARSE_TPB, 0, stream>>>(q_idx, w, group_sum, n_entries, Q, Hi, cap, top_groups,
+                                                         gsel, gcount);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

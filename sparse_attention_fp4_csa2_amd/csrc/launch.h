@@ -25,6 +25,12 @@ struct KeyCache {
   const uint8_t* scales;
 };
 
+// csa2_index_topk / _key8 after their pointer checks: argument checks against
+// the sizes, workspace carving and the launches; returns a CSA2 status.
+int index_topk_run(const uint16_t* q_idx, const float* w, const KeyCache& keys, const float* group_sum,
+                   const int32_t* n_entries, const int32_t* q_pos, int B, int Q, int Hi, int cap, int top_k,
+                   int top_groups, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
+
 // Block scores fp32 [rows][n_out]: flat (gsel == nullptr: n_out = cap/8) or
 // restricted to the selected groups gsel [rows][n_groups_sel] (n_out = 64 per group).
 int launch_index_scores(const uint16_t* q_idx, const float* w, const KeyCache& keys,
@@ -32,10 +38,12 @@ int launch_index_scores(const uint16_t* q_idx, const float* w, const KeyCache& k
                         int cap, const int32_t* gsel, int n_groups_sel, float* scores,
                         hipStream_t stream);
 
-// Coarse group scores fp32 [rows][cap/512] from group sums.
-int launch_group_scores(const uint16_t* q_idx, const float* w, const float* group_sum,
-                        const int32_t* n_entries, int B, int Q, int Hi, int cap, float* gscores,
-                        hipStream_t stream);
+// Coarse stage of the two-level indexer in one launch: group scores from the
+// group sums and the top_groups best groups per row -> gsel [rows][top_groups]
+// (ascending, -1 padded), gcount [rows].  cap / 512 <= 1024.
+int launch_coarse_select(const uint16_t* q_idx, const float* w, const float* group_sum,
+                         const int32_t* n_entries, int B, int Q, int Hi, int cap, int top_groups, int32_t* gsel,
+                         int32_t* gcount, hipStream_t stream);
 
 // Top-k per row of scores [rows][n] -> idx [rows][k] ascending, -1 padded, count [rows].
 // With gsel != nullptr, position p maps to block gsel[row][p / 64] * 64 + p % 64.

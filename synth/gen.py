@@ -3,8 +3,9 @@
 All float inputs are drawn as float32 N(0, 1) from NumPy's PCG64 and rounded to
 bfloat16 with round-to-nearest-even; indexer weights stay float32.  Planting
 only edits indexer keys (never the latent): one entry of each planted block gets
-the key c * q_h* (h* = the indexer head with the largest weight), so that
-block's score stands clear of the unplanted ones.  ``plant_tight`` instead puts
+the key c_r * q_h* (h* = the indexer head with the largest weight, c_r a
+multiplier of its own between c and 2c), so that block's score stands clear of
+the unplanted ones and the planted scores are spread, not one shared value.  ``plant_tight`` instead puts
 the planted scores just above the best unplanted block, using a scoring
 function supplied by the caller.
 """
@@ -111,14 +112,24 @@ def _entry_in_block(rng, blk, n_entries):
     return 8 * blk + int(rng.integers(0, hi))
 
 
-def plant_dominant(keys, n_entries, q_idx_row, w_row, blocks, rng, c=3.0):
-    """In place: one present entry of each block in ``blocks`` gets key bf16(c * q_h*)."""
+def plant_dominant(keys, n_entries, q_idx_row, w_row, blocks, rng, c=3.0, spread=1.0):
+    """In place: one present entry of each block in ``blocks`` gets key bf16(c_r * q_h*).
+
+    The planted blocks take distinct multipliers c_r = c * (1 + spread * r / n) for
+    r = 0 .. n-1 in a seeded random order, so their scores (positively
+    homogeneous in the key) spread over [c, c * (1 + spread)) times the score of
+    q_h* instead of sharing one value.  The key is rounded to bf16 (a relative
+    step of 2^-8 .. 2^-7), so runs of about n / (2^7 spread) .. n / (2^8 spread)
+    neighbouring multipliers share one key and tie.
+    """
     h = _lead_head(w_row)
     u = bf16_to_f32(q_idx_row[h])
-    key = bf16_rne(np.float32(c) * u)
-    for b in blocks:
+    blocks = np.asarray(blocks)
+    n = max(len(blocks), 1)
+    for r, b in enumerate(rng.permutation(blocks)):
+        key = bf16_rne(np.float32(c * (1.0 + spread * r / n)) * u)
         keys[_entry_in_block(rng, int(b), n_entries)] = key
-    return np.asarray(blocks)
+    return blocks
 
 
 def plant_tight(keys, n_entries, q_idx_row, w_row, blocks, rng, score_fn, margin=0.5, step=0.01):
@@ -269,8 +280,10 @@ def prefill_inputs(cfg, seed=None, q_rows=None, n_dirs=4, c=3.0, beta=1.0):
     for d in range(n_dirs):
         blocks = choose_blocks(rng, nb_prior, cfg.K, exclude=used)
         used = np.concatenate([used, blocks])
-        key = bf16_rne(np.float32(c) * bf16_to_f32(dirs[d]))
-        for b in blocks:
+        v = bf16_to_f32(dirs[d])
+        # distinct multipliers per planted block, as in plant_dominant
+        for r, b in enumerate(rng.permutation(blocks)):
+            key = bf16_rne(np.float32(c * (1.0 + r / len(blocks))) * v)
             keys[0, _entry_in_block(rng, int(b), prior)] = key
         planted.append(blocks)
     swa_total = cfg.W + Q

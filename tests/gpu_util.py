@@ -38,11 +38,17 @@ def assert_close_rms(got, ref, frac=1e-2, what="output"):
     return err / rms
 
 
-def assert_lse_close(got, ref, tol=1e-3):
+def assert_lse_close(got, ref, tol=1e-3, rel=0.0):
+    """|got - ref| <= tol + rel * max|ref| over the finite entries (the -inf pattern must match).
+
+    ``rel`` scales the bound with the logits for workloads whose logits are far
+    from O(1) (their fp32 logits carry an error relative to their size)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     fin = np.isfinite(ref)
     assert (np.isfinite(got) == fin).all(), "lse: -inf pattern differs"
     if fin.any():
         err = np.abs(got[fin] - ref[fin]).max()
-        assert err <= tol, f"lse: max|err| {err:.3e} > {tol}"
+        bound = tol + rel * np.abs(ref[fin]).max()
+        print(f"[parity] lse: max|err| = {err:.3e} (bound {bound:.3e}, max|lse| {np.abs(ref[fin]).max():.1f})")
+        assert err <= bound, f"lse: max|err| {err:.3e} > {bound:.3e}"

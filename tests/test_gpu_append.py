@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import indexer, mxfp4
+from oracle import indexer, mxfp4, mxfp8
 from synth import CONFIGS, normal_bf16, rng_for
 from tests import pins
 from tests.gpu_util import dev, dev_bf16, host
@@ -78,15 +78,25 @@ def test_special_groups_bit_exact():
     assert np.array_equal(host(cache)[0], ref)
 
 
+def _oracle_group_sums(keys_u16, n_entries, cap):
+    """fp32 group sums the GPU must hold: the oracle's group mean times the present count."""
+    means, present = indexer.group_means(keys_u16, n_entries, n_groups=cap // 512)
+    cnt = np.clip(n_entries - 512 * np.arange(cap // 512), 0, 512)
+    return (means * cnt[:, None]).astype(np.float32), present
+
+
 def test_ragged_appends_keys_and_group_sums():
+    # append, overwrite the tail across a group boundary, overwrite inside a
+    # group, run past capacity: each touched group's sum is recomputed from the
+    # keys the cache holds, so an overwritten key counts once, with its new value
     rng = rng_for(21)
-    B, cap = 3, 2048
+    B, cap = 4, 2048
     first = normal_bf16(rng, (B, 700, 512))
     kfirst = normal_bf16(rng, (B, 700, 64))
-    cache, kc, gs = _append(first, cap, start=[0, 0, 0], keys=kfirst, with_groups=True)
+    cache, kc, gs = _append(first, cap, start=[0] * B, keys=kfirst, with_groups=True)
     second = normal_bf16(rng, (B, 37, 512))
     ksecond = normal_bf16(rng, (B, 37, 64))
-    starts = [700, 690, 2040]                  # append, overwrite tail, run past capacity
+    starts = [700, 500, 2040, 100]
     _append(second, cap, start=starts, keys=ksecond, with_groups=True, cache=cache,
             key_cache=kc, gsum=gs)
     got = host(cache)
@@ -105,15 +115,37 @@ def test_ragged_appends_keys_and_group_sums():
             mxfp4.write_records(ref, lat[lo:hi], lo)
         assert np.array_equal(got[b], ref), f"seq {b}"
         assert np.array_equal(gotk[b][written], keys[written])
-        # group sums: every appended key added once (overwrites add again)
-        exp = np.zeros((cap // 512, 64))
-        kf = pins_f64(kfirst[b])
-        for j in range(700):
-            exp[j // 512] += kf[j]
-        kf2 = pins_f64(ksecond[b])
-        for i in range(n2):
-            exp[(s + i) // 512] += kf2[i]
-        assert np.allclose(gsum[b], exp, rtol=1e-5, atol=1e-3)
+        n_ent = int(np.nonzero(written)[0].max()) + 1
+        exp, _ = _oracle_group_sums(keys[:n_ent], n_ent, cap)
+        assert np.array_equal(gsum[b], exp), f"seq {b}: group sums differ at " \
+            f"{np.argwhere(gsum[b] != exp)[:4].tolist()}"
+
+
+def test_repeated_overwrites_keep_group_sums():
+    # the decode step rewrites one entry again and again: its group's sum must
+    # stay the sum of the keys held (bf16 and MXFP8 key caches)
+    rng = rng_for(22)
+    B, cap, n = 2, 1024, 1000
+    lat = normal_bf16(rng, (B, n, 512))
+    keys = normal_bf16(rng, (B, n, 64))
+    cache, kc, gs = _append(lat, cap, keys=keys, with_groups=True)
+    lib = _lib()
+    k8 = torch.zeros(B, cap, 64, dtype=torch.uint8, device="cuda")
+    ks = torch.zeros(B, cap, 2, dtype=torch.uint8, device="cuda")
+    gs8 = torch.zeros(B, cap // 512, 64, dtype=torch.float32, device="cuda")
+    lib.append_key8(dev_bf16(keys), dev(np.zeros(B, np.int32)), k8, ks, group_sum=gs8)
+    last = dev(np.full(B, n - 1, np.int32))
+    new_lat, new_key = dev_bf16(lat[:, n - 1:]), dev_bf16(keys[:, n - 1:])
+    for _ in range(200):
+        lib.append_fp4(new_lat, last, cache, idx_key=new_key, key_cache=kc, group_sum=gs)
+        lib.append_key8(new_key, last, k8, ks, group_sum=gs8)
+    torch.cuda.synchronize()
+    for b in range(B):
+        exp, _ = _oracle_group_sums(keys[b], n, cap)
+        assert np.array_equal(host(gs)[b], exp), f"bf16 keys, seq {b}"
+        deq = mxfp8.quantize_dequantize(keys[b])
+        exp8, _ = _oracle_group_sums(deq, n, cap)
+        assert np.array_equal(host(gs8)[b], exp8), f"MXFP8 keys, seq {b}"
 
 
 def _runs(mask):
@@ -128,10 +160,6 @@ def _runs(mask):
         else:
             j += 1
     return out
-
-
-def pins_f64(bits):
-    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def test_decode_single_entry_append():

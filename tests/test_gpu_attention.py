@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from oracle import attention, modes, mxfp4
-from synth import CONFIGS, decode_inputs, normal_bf16, rng_for
+from synth import CONFIGS, bf16_rne, bf16_to_f32, decode_inputs, normal_bf16, rng_for
 from tests.gpu_util import assert_close_rms, assert_lse_close, dev, dev_bf16, host
 
 pytestmark = pytest.mark.gpu
@@ -447,3 +447,56 @@ def test_attend_layer_extreme_magnitudes():
         ro, rl = modes.attend_row(q[b, 0], cache_np[b], idx[b, 0], K, N, swa[b], Lw, W)
         assert_close_rms(out[b, 0], ro, what=f"row {b} (2^{ks[b]})")
         assert_lse_close(lse[b, 0], rl)
+
+
+@pytest.mark.parametrize("factor", [16, 64, 256, 1024, 4096])
+def test_outlier_query_channels(factor):
+    # one channel per 32-dim block of every head's query at `factor` times the
+    # rest (H 64, K 2048 blocks = 16384 entries): blocks this wide keep few bits
+    # of their bulk in three FP6 terms, so from about 2^4 x a wave switches to
+    # the exact two-term FP8 query; the output must stay within the bar
+    rng = rng_for(300 + factor)
+    B, N, H, K = 2, 20000, 64, 2048
+    lat = normal_bf16(rng, (B, N, 512))
+    qf = bf16_to_f32(normal_bf16(rng, (B, 1, H, 512))).reshape(B, 1, H, 16, 32)
+    cols = rng.integers(0, 32, size=(B, 1, H, 16))
+    np.put_along_axis(qf, cols[..., None], np.take_along_axis(qf, cols[..., None], -1) * factor, -1)
+    if factor >= 1024:
+        # logits that large leave one entry per head; scale the whole query down so
+        # the softmax keeps many entries and the bulk channels decide their order
+        qf = qf * np.float32(64.0 / factor)
+    q = bf16_rne(qf.reshape(B, 1, H, 512))
+    nbp = (N + 7) // 8
+    idx = np.stack([np.sort(rng.choice(nbp, K, replace=False)) for _ in range(B)])[:, None].astype(np.int32)
+    count = np.full((B, 1), K, np.int32)
+    ne = np.full(B, N, np.int32)
+    o, l = gpu_sparse(q, gpu_cache(lat, N), idx, count, ne)
+    cache_np = np.stack([mxfp4.build_records(lat[b], N) for b in range(B)])
+    ro, rl = oracle_rows(q, cache_np, idx, count, ne)
+    assert_close_rms(o, ro, what=f"outlier x{factor} out")
+    # logits here reach ~60 (the outlier channels dominate q.K): the lse bound
+    # takes a part relative to their size; the output bar above is unchanged
+    assert_lse_close(l, rl, rel=1e-4)
+
+
+def test_outlier_query_mixed_waves():
+    # outliers only in dims 0..127 of head group 0 (wave 0 of those workgroups
+    # takes the FP8 form, the other waves and head group 1 stay FP6), several
+    # splits, ragged counts
+    rng = rng_for(310)
+    B, N, H, K = 3, 9000, 64, 600
+    lat = normal_bf16(rng, (B, N, 512))
+    qf = bf16_to_f32(normal_bf16(rng, (B, 1, H, 512)))
+    qf[:, :, :32, 0:128:32] *= np.float32(2048.0)
+    q = bf16_rne(qf)
+    nbp = (N + 7) // 8
+    count = np.array([[K], [311], [1]], np.int32)
+    idx = np.full((B, 1, K), -1, np.int32)
+    for b in range(B):
+        idx[b, 0, :count[b, 0]] = np.sort(rng.choice(nbp, count[b, 0], replace=False))
+    ne = np.full(B, N, np.int32)
+    o, l = gpu_sparse(q, gpu_cache(lat, N), idx, count, ne)
+    cache_np = np.stack([mxfp4.build_records(lat[b], N) for b in range(B)])
+    ro, rl = oracle_rows(q, cache_np, idx, count, ne)
+    assert_close_rms(o, ro, what="mixed FP6 / FP8 waves out")
+    assert_lse_close(l, rl, rel=1e-4)

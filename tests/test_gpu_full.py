@@ -149,7 +149,20 @@ def test_mxfp8_key_cache_full_size(name):
 
 @pytest.mark.timeout(600)
 def test_decode1m_two_level_full_size():
+    # the bench's step loop (its decode append rewrites entry N-1 every step)
+    # for 1000 more steps: the group sums must still be the sums of the keys the
+    # cache holds, and the two-level selection the oracle's
     cfg, (x, layers), wl = _workload("decode1m")
+    for _ in range(1000):
+        wl.step()
+    torch.cuda.synchronize()
+    got = host(wl.cache.group_sum)
+    G = cfg.cap // 512
+    for b in range(cfg.B):
+        means, _ = indexer.group_means(x.keys[b], int(x.n_entries[b]), n_groups=G)
+        cnt = np.clip(int(x.n_entries[b]) - 512 * np.arange(G), 0, 512)
+        exp = (means * cnt[:, None]).astype(np.float32)
+        assert np.array_equal(got[b], exp), f"seq {b}: group sums differ after 1002 steps"
     _decode_checks(cfg, x, layers, wl, rows=list(range(cfg.B)))
 
 
