@@ -530,8 +530,8 @@ def main():
         "config": res["config"],
         "timing": ("value: cold steps (each after a 1 GiB scratch read that evicts L2 and the last-level "
                    "cache; HIP events around the step); warm_value: the same steps back to back"),
-        "compute": ("Q.K on the scaled FP4 x FP6 MFMA (query split into three E2M3 terms; two exact E4M3 "
-                    "terms on FP4 x FP8 for query blocks with outlier channels), P.V on fp16 MFMA with the "
+        "compute": ("Q.K on the scaled FP4 x FP6 MFMA (query split into three E2M3 terms; bf16 MFMA on exactly "
+                    "dequantised codes for query blocks with outlier channels), P.V on fp16 MFMA with the "
                     "MXFP4 values dequantised to fp16, fp32 accumulate; window in bf16"),
     }
     for k, v in res.items():
