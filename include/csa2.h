@@ -58,7 +58,8 @@ enum {
     CSA2_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misaligned buffer   */
     CSA2_ERR_UNSUPPORTED = -2,   /* valid but not supported by these kernels    */
     CSA2_ERR_WS_TOO_SMALL = -3,  /* workspace smaller than the *_ws() query      */
-    CSA2_ERR_LAUNCH = -4         /* the HIP runtime reported a launch error      */
+    CSA2_ERR_LAUNCH = -4,        /* the HIP runtime reported a launch error      */
+    CSA2_ERR_SCRATCH_LIMIT = -5  /* needs more than a static scratch array holds */
 };
 
 /* Append n_new entries per sequence to the latent cache (MXFP4 quantise + pack).
@@ -114,6 +115,24 @@ int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* key_c
                     int B, int Q, int Hi, int cap, int top_k, int top_groups,
                     int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_index_topk_ws(int B, int Q, int cap, int top_groups);
+
+/* csa2_index_topk for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, rule, outputs and errors as csa2_index_topk, without ws /
+ * ws_bytes: the selection's scratch is a static device array of
+ * CSA2_INDEX_SCRATCH_BYTES per GPU (held until the process ends), and the call
+ * allocates nothing.  A call whose csa2_index_topk_ws(B, Q, cap, top_groups)
+ * exceeds it returns CSA2_ERR_SCRATCH_LIMIT before anything is enqueued (8 MiB
+ * covers 2M block scores: every decode workload here; a 4096-row prefill does
+ * not fit).  The scratch used is the current device's (the stream must belong
+ * to it); nothing in it needs clearing between calls.  Calls that overlap on one
+ * GPU (other streams, or unordered host threads) share that scratch and race:
+ * order them. */
+#define CSA2_INDEX_SCRATCH_BYTES ((size_t)8 << 20)
+int csa2_index_topk_noalloc(const uint16_t* q_idx, const float* w, const uint16_t* key_cache,
+                            const float* group_sum, const int32_t* n_entries, const int32_t* q_pos,
+                            int B, int Q, int Hi, int cap, int top_k, int top_groups,
+                            int32_t* idx, int32_t* count, void* stream);
 
 /* Lower-precision indexer key cache: the keys in MXFP8 (OCP Microscaling
  * v1.0, E4M3 elements -- bias 7, subnormals, largest finite 448, no

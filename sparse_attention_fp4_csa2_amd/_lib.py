@@ -26,6 +26,7 @@ _SIGS = {
     "csa2_append_fp4": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
     "csa2_index_topk": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "csa2_index_topk_ws": (_SZ, [_I, _I, _I, _I]),
+    "csa2_index_topk_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "csa2_append_key8": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
     "csa2_index_topk_key8": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "csa2_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
@@ -133,6 +134,21 @@ def index_topk(q_idx, w, key_cache, n_entries, top_k, idx, count, ws, group_sum=
                              _ptr(idx, torch.int32, "idx"), _ptr(count, torch.int32, "count"),
                              _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "csa2_index_topk")
+
+
+def index_topk_noalloc(q_idx, w, key_cache, n_entries, top_k, idx, count, group_sum=None, q_pos=None,
+                       top_groups=0, stream=None):
+    """csa2_index_topk_noalloc: csa2_index_topk with its scratch in the library's static per-GPU array."""
+    lib = load()
+    B, Q, Hi = q_idx.shape[0], q_idx.shape[1], q_idx.shape[2]
+    cap = key_cache.shape[1]
+    rc = lib.csa2_index_topk_noalloc(_bf16_ptr(q_idx, "q_idx"), _ptr(w, torch.float32, "w"),
+                                     _bf16_ptr(key_cache, "key_cache"), _ptr(group_sum, torch.float32, "group_sum"),
+                                     _ptr(n_entries, torch.int32, "n_entries"), _ptr(q_pos, torch.int32, "q_pos"),
+                                     B, Q, Hi, cap, top_k, top_groups,
+                                     _ptr(idx, torch.int32, "idx"), _ptr(count, torch.int32, "count"),
+                                     _stream(stream))
+    _check(rc, "csa2_index_topk_noalloc")
 
 
 def append_key8(idx_key, start_entry, key8, key8_scale, group_sum=None, latent=None, cache=None, stream=None):

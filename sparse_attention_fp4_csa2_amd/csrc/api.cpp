@@ -95,6 +95,7 @@ const char* csa2_status_str(int status) {
     case CSA2_ERR_UNSUPPORTED: return "unsupported configuration";
     case CSA2_ERR_WS_TOO_SMALL: return "workspace too small";
     case CSA2_ERR_LAUNCH: return "kernel launch failed";
+    case CSA2_ERR_SCRATCH_LIMIT: return "request exceeds the static scratch";
     default: return "unknown status";
   }
 }
