@@ -89,14 +89,14 @@ __device__ __forceinline__ void write_key8(const uint16_t* __restrict__ idx_key,
 
 // One wave per new entry: the latent's MXFP4 record bytes (latent may be
 // null: keys only), and its indexer key as bf16 (key_cache) or MXFP8 (key8).
-__global__ __launch_bounds__(256) void append_fp4_kernel(
+// Workgroup x of sequence b takes new entries 4x .. 4x + 3.
+__device__ __forceinline__ void append_entries(
     const uint16_t* __restrict__ latent, const uint16_t* __restrict__ idx_key,
     const int32_t* __restrict__ start_entry, int n_new, int cap,
     uint8_t* __restrict__ cache, uint16_t* __restrict__ key_cache,
-    uint8_t* __restrict__ key8, uint8_t* __restrict__ key8_scale) {
-  const int b = blockIdx.y;
+    uint8_t* __restrict__ key8, uint8_t* __restrict__ key8_scale, int x, int b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + wave;          // new entry index
+  const int i = x * 4 + wave;                   // new entry index
   if (i >= n_new) return;
   const long long j = (long long)start_entry[b] + i;   // cache entry position
   if (j < 0 || j >= cap) return;
@@ -144,56 +144,74 @@ __device__ __forceinline__ float e4m3_value(uint32_t c, int sb) {
   return ldexpf((c & 0x80u) ? -mag : mag, sb - 127);
 }
 
-// Group sums, recomputed after the append for every 512-entry group it
-// touched: the sum of the keys held in all 512 slots of the group (slots that
-// hold no entry are zero in a zero-initialised cache), read back from the key
-// cache, so an overwritten entry counts once with its new key.  One 256-thread
-// block per (sequence, touched group): thread t sums dims [8(t%8), +8) over the
-// slots t/8, t/8 + 32, ... in fp64, and the 32 partials meet in LDS in a fixed
-// order.  fp64 holds the sum of 512 bf16 (or E4M3 x 2^k) values exactly unless
-// they span more than ~40 binades, so the stored fp32 is the exact sum rounded
-// once, whatever the order.
+// Group sums, recomputed for every 512-entry group the append touches: the sum
+// of the keys all 512 slots of the group hold once the append is done (slots
+// that hold no entry are zero in a zero-initialised cache), so an overwritten
+// entry counts once, with its new key.  A slot the append writes is read from
+// the new keys themselves (MXFP8: quantised here exactly as the entry waves
+// quantise it), every other slot from the key cache, so these workgroups share
+// the append's launch without reading what its other workgroups write.  One
+// 256-thread workgroup per (sequence, touched group gi): thread t sums dims
+// [8(t%8), +8) over the slots t/8, t/8 + 32, ... in fp64, and the 32 partials
+// meet in LDS in a fixed order.  fp64 holds the sum of 512 bf16 (or E4M3 x 2^k)
+// values exactly unless they span more than ~40 binades, so the stored fp32 is
+// the exact sum rounded once, whatever the order.
 template <bool K8>
-__global__ __launch_bounds__(256) void group_sum_kernel(
-    const uint16_t* __restrict__ key_cache, const uint8_t* __restrict__ key8,
-    const uint8_t* __restrict__ key8_scale, const int32_t* __restrict__ start_entry, int n_new, int cap,
-    float* __restrict__ group_sum) {
+__device__ __forceinline__ void group_sum_unit(
+    const uint16_t* __restrict__ idx_key, const uint16_t* __restrict__ key_cache,
+    const uint8_t* __restrict__ key8, const uint8_t* __restrict__ key8_scale,
+    const int32_t* __restrict__ start_entry, int n_new, int cap, float* __restrict__ group_sum, int gi, int b) {
   __shared__ double part[32][DI + 1];
-  const int b = blockIdx.y;
   const int t = threadIdx.x, c = t & 7, r = t >> 3;
   const long long s0 = start_entry[b];
   const long long first = max(s0, 0LL), last = min(s0 + n_new, (long long)cap);   // written [first, last)
   if (first >= last) return;
-  const long long g = first / GROUP_ENTRIES + blockIdx.x;
+  const long long g = first / GROUP_ENTRIES + gi;
   if (g * GROUP_ENTRIES >= last) return;
   double acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.0;
-  const size_t e0 = (size_t)b * cap + (size_t)g * GROUP_ENTRIES;
   constexpr int PER = GROUP_ENTRIES / 32;      // slots per thread, all requested before any is summed
-  if constexpr (K8) {
-    uint2 cw[PER];
-    int sbv[PER];
+  uint4 kw[PER];      // bf16 key words (new slot, or bf16 cache); MXFP8 cache: codes in .x .y, scale in .z
+  bool fresh[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const size_t e = e0 + (size_t)(r + 32 * i);
-      cw[i] = *reinterpret_cast<const uint2*>(key8 + e * DI + 8 * c);
-      sbv[i] = key8_scale[e * 2 + (c >> 2)];
+  for (int i = 0; i < PER; ++i) {
+    const long long j = g * GROUP_ENTRIES + r + 32 * i;
+    fresh[i] = j >= first && j < last;
+    const size_t e = (size_t)b * cap + (size_t)j;
+    if (fresh[i]) {
+      kw[i] = *reinterpret_cast<const uint4*>(idx_key + ((size_t)b * n_new + (size_t)(j - s0)) * DI + 8 * c);
+    } else if constexpr (K8) {
+      const uint2 cw = *reinterpret_cast<const uint2*>(key8 + e * DI + 8 * c);
+      kw[i] = make_uint4(cw.x, cw.y, key8_scale[e * 2 + (c >> 2)], 0u);
+    } else {
+      kw[i] = *reinterpret_cast<const uint4*>(key_cache + e * DI + 8 * c);
     }
+  }
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint32_t w2[2] = {cw[i].x, cw[i].y};
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t w4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+    if constexpr (K8) {
+      // a new key's 32-dim scale group spans the 4 threads c = 4(c/4) .. +3 of this slot
+      uint32_t amax = 0;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] += (double)e4m3_value((w2[k >> 2] >> (8 * (k & 3))) & 0xFFu, sbv[i]);
-    }
-  } else {
-    uint4 kw[PER];
+      for (int k = 0; k < 8; ++k) amax = max(amax, ((k & 1) ? (w4[k >> 1] >> 16) : w4[k >> 1]) & 0x7FFFu);
+      amax = fresh[i] ? amax : 0u;
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
+      const int sb_new = amax ? min(max(floor_log2_bf16(amax) - 8 + 127, 0), 254) : 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-      kw[i] = *reinterpret_cast<const uint4*>(key_cache + (e0 + (size_t)(r + 32 * i)) * DI + 8 * c);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint32_t w4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+      for (int k = 0; k < 8; ++k) {
+        float v;
+        if (fresh[i]) {
+          const uint32_t h = ((k & 1) ? (w4[k >> 1] >> 16) : w4[k >> 1]) & 0xFFFFu;
+          v = e4m3_value(((h >> 15) << 7) | e4m3_code(h & 0x7FFFu, sb_new), sb_new);
+        } else {
+          v = e4m3_value((w4[k >> 2] >> (8 * (k & 3))) & 0xFFu, (int)w4[2]);
+        }
+        acc[k] += (double)v;
+      }
+    } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         acc[k] += (double)__uint_as_float((k & 1) ? (w4[k >> 1] & 0xFFFF0000u) : (w4[k >> 1] << 16));
@@ -203,36 +221,56 @@ __global__ __launch_bounds__(256) void group_sum_kernel(
   for (int k = 0; k < 8; ++k) part[r][8 * c + k] = acc[k];
   __syncthreads();
   if (t < DI) {
-    double s = 0.0;
-    for (int i = 0; i < 32; ++i) s += part[i][t];
-    group_sum[((size_t)b * (cap / GROUP_ENTRIES) + (size_t)g) * DI + t] = (float)s;
+    double sum = 0.0;
+    for (int i = 0; i < 32; ++i) sum += part[i][t];
+    group_sum[((size_t)b * (cap / GROUP_ENTRIES) + (size_t)g) * DI + t] = (float)sum;
   }
+}
+
+// One launch per append: workgroups [0, n_entry_wg) of each sequence write the
+// new entries, the rest recompute the touched groups' sums (when group_sum is
+// given).
+template <bool K8>
+__global__ __launch_bounds__(256) void append_kernel(
+    const uint16_t* __restrict__ latent, const uint16_t* __restrict__ idx_key,
+    const int32_t* __restrict__ start_entry, int n_new, int cap, uint8_t* __restrict__ cache,
+    uint16_t* __restrict__ key_cache, uint8_t* __restrict__ key8, uint8_t* __restrict__ key8_scale,
+    float* __restrict__ group_sum, int n_entry_wg) {
+  const int b = blockIdx.y;
+  if ((int)blockIdx.x < n_entry_wg)
+    append_entries(latent, idx_key, start_entry, n_new, cap, cache, key_cache, key8, key8_scale, blockIdx.x, b);
+  else
+    group_sum_unit<K8>(idx_key, key_cache, key8, key8_scale, start_entry, n_new, cap, group_sum,
+                       (int)blockIdx.x - n_entry_wg, b);
+}
+
+static int launch_append_t(bool k8, const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry,
+                           int B, int n_new, int cap, uint8_t* cache, uint16_t* key_cache, uint8_t* key8,
+                           uint8_t* key8_scale, float* group_sum, hipStream_t stream) {
+  const int n_entry_wg = (n_new + 3) / 4;
+  const int n_group_wg = group_sum ? (n_new + GROUP_ENTRIES - 1) / GROUP_ENTRIES + 1 : 0;
+  dim3 grid(n_entry_wg + n_group_wg, B);
+  if (k8)
+    append_kernel<true><<<grid, 256, 0, stream>>>(latent, idx_key, start_entry, n_new, cap, cache, nullptr, key8,
+                                                  key8_scale, group_sum, n_entry_wg);
+  else
+    append_kernel<false><<<grid, 256, 0, stream>>>(latent, idx_key, start_entry, n_new, cap, cache, key_cache,
+                                                   nullptr, nullptr, group_sum, n_entry_wg);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 int launch_append_key8(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry, int B,
                        int n_new, int cap, uint8_t* cache, uint8_t* key8, uint8_t* key8_scale, float* group_sum,
                        hipStream_t stream) {
-  dim3 grid((n_new + 3) / 4, B);
-  append_fp4_kernel<<<grid, 256, 0, stream>>>(latent, idx_key, start_entry, n_new, cap, cache, nullptr, key8,
-                                              key8_scale);
-  if (group_sum != nullptr) {
-    dim3 g2((n_new + GROUP_ENTRIES - 1) / GROUP_ENTRIES + 1, B);
-    group_sum_kernel<true><<<g2, 256, 0, stream>>>(nullptr, key8, key8_scale, start_entry, n_new, cap, group_sum);
-  }
-  return hipGetLastError() == hipSuccess ? 0 : -4;
+  return launch_append_t(true, latent, idx_key, start_entry, B, n_new, cap, cache, nullptr, key8, key8_scale,
+                         group_sum, stream);
 }
 
 int launch_append(const uint16_t* latent, const uint16_t* idx_key, const int32_t* start_entry,
                   int B, int n_new, int cap, uint8_t* cache, uint16_t* key_cache,
                   float* group_sum, hipStream_t stream) {
-  dim3 grid((n_new + 3) / 4, B);
-  append_fp4_kernel<<<grid, 256, 0, stream>>>(latent, idx_key, start_entry, n_new, cap, cache,
-                                              key_cache, nullptr, nullptr);
-  if (group_sum != nullptr) {
-    dim3 g2((n_new + GROUP_ENTRIES - 1) / GROUP_ENTRIES + 1, B);
-    group_sum_kernel<false><<<g2, 256, 0, stream>>>(key_cache, nullptr, nullptr, start_entry, n_new, cap, group_sum);
-  }
-  return hipGetLastError() == hipSuccess ? 0 : -4;
+  return launch_append_t(false, latent, idx_key, start_entry, B, n_new, cap, cache, key_cache, nullptr, nullptr,
+                         group_sum, stream);
 }
 
 }  // namespace csa2

@@ -285,56 +285,47 @@ __global__ __launch_bounds__(256) void index_rows_kernel(
 
 // Two-level stage, coarse part, in one launch: one 1024-thread workgroup per
 // query row, thread g = group g.  Each thread requests its group's 64 summed
-// key dims at once (one round of memory latency for the whole row), takes the
-// mean (sum / present count), and forms sum_h w_h max(0, q_h . mean) with the
-// row's indexer query read from LDS (fp32, staged once); the scores meet in LDS
-// and the radix select of the top-K kernels keeps the best top_groups groups
-// (ascending ids, -1 padded, with their count).  G = cap / 512 <= 1024
-// (cap / 8 <= 65536).
+// key dims at once (one round of memory latency for the whole row) and forms
+// sum_h w_h max(0, q_h . sum / count) (count = the group's present entries).
+// The row's indexer query is the same for every thread: it is read through
+// the scalar unit (a uniform address in the constant address space), so each
+// query value is one scalar operand of the threads' FMAs instead of a vector
+// read per thread.  The radix select of the top-K kernels then keeps the best
+// top_groups groups (ascending ids, -1 padded, with their count), with digits
+// relative to the row's score range (group scores share a few exponents, so
+// fixed top-bit digits would take several passes).  G = cap / 512 <= 1024 (cap / 8 <= 65536).
 constexpr int COARSE_TPB = 1024;
+typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
 
 __global__ __launch_bounds__(COARSE_TPB) void coarse_select_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const float* __restrict__ group_sum,
     const int32_t* __restrict__ n_entries, int Q, int Hi, int cap, int top_groups, int32_t* __restrict__ gsel,
     int32_t* __restrict__ gcount) {
-  __shared__ float4 qs[MAX_HI][DI / 4];
-  __shared__ float ws[MAX_HI];
   const int row = blockIdx.x, b = row / Q;
   const int G = cap / GROUP_ENTRIES;
   const int ne = min(n_entries[b], cap);
-  const int t = threadIdx.x;
-  const int g = t;
+  const int g = threadIdx.x;
   const int cnt = g < G ? min(GROUP_ENTRIES, ne - g * GROUP_ENTRIES) : 0;
   float4 m4[DI / 4];
-  if (cnt > 0) {
-    const float4* gs = reinterpret_cast<const float4*>(group_sum + ((size_t)b * G + g) * DI);
+  const float4* gs = reinterpret_cast<const float4*>(group_sum + ((size_t)b * G + min(g, G - 1)) * DI);
 #pragma unroll
-    for (int d4 = 0; d4 < DI / 4; ++d4) m4[d4] = gs[d4];
-  }
-  if (t < Hi * (DI / 4)) {
-    const int h = t / (DI / 4), d4 = t % (DI / 4);
-    const uint2 qq = *reinterpret_cast<const uint2*>(q_idx + ((size_t)row * Hi + h) * DI + 4 * d4);
-    qs[h][d4] = make_float4(__uint_as_float(qq.x << 16), __uint_as_float(qq.x & 0xFFFF0000u),
-                            __uint_as_float(qq.y << 16), __uint_as_float(qq.y & 0xFFFF0000u));
-  }
-  if (t < Hi) ws[t] = w[(size_t)row * Hi + t];
-  __syncthreads();
-  float s = -__builtin_inff();
-  if (cnt > 0) {
-    const float inv = 1.f / (float)cnt;
-    s = 0.f;
-    for (int h = 0; h < Hi; ++h) {
-      float dot = 0.f;
+  for (int d4 = 0; d4 < DI / 4; ++d4) m4[d4] = gs[d4];
+  const const_u32_ptr qrow = (const_u32_ptr)(const void*)(q_idx + (size_t)row * Hi * DI);
+  const const_u32_ptr wrow = (const_u32_ptr)(const void*)(w + (size_t)row * Hi);
+  const float inv = cnt > 0 ? 1.f / (float)cnt : 0.f;
+  float s = 0.f;
+  for (int h = 0; h < Hi; ++h) {
+    float dot = 0.f;
 #pragma unroll
-      for (int d4 = 0; d4 < DI / 4; ++d4) {
-        const float4 q4 = qs[h][d4];
-        dot += q4.x * m4[d4].x + q4.y * m4[d4].y + q4.z * m4[d4].z + q4.w * m4[d4].w;
-      }
-      s += ws[h] * fmaxf(dot * inv, 0.f);
+    for (int d4 = 0; d4 < DI / 4; ++d4) {
+      const uint32_t q01 = qrow[h * (DI / 2) + 2 * d4], q23 = qrow[h * (DI / 2) + 2 * d4 + 1];
+      dot += __uint_as_float(q01 << 16) * m4[d4].x + __uint_as_float(q01 & 0xFFFF0000u) * m4[d4].y +
+             __uint_as_float(q23 << 16) * m4[d4].z + __uint_as_float(q23 & 0xFFFF0000u) * m4[d4].w;
     }
+    s += __uint_as_float(wrow[h]) * fmaxf(dot * inv, 0.f);
   }
-  uint32_t key[1] = {g < G ? score_key(s) : 0u};
-  sel::select_core<COARSE_TPB, 1, false>(key, G, top_groups, nullptr, 0, row, gsel + (size_t)row * top_groups,
+  uint32_t key[1] = {cnt > 0 ? score_key(s) : 0u};
+  sel::select_core<COARSE_TPB, 1, true>(key, G, top_groups, nullptr, 0, row, gsel + (size_t)row * top_groups,
                                          gcount + row);
 }
 

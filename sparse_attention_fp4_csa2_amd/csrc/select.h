@@ -9,7 +9,7 @@ namespace sel {
 
 
 constexpr int HIST_BINS = 2048;
-constexpr uint32_t RANK_MAX = 64;   // a boundary bin this small is ranked directly
+constexpr uint32_t RANK_MAX = 256;   // a boundary bin this small is ranked directly
 
 // Wave-wide inclusive prefix sum: four DPP row shifts (1, 2, 4, 8) within each
 // 16-lane row, then row broadcasts of lane 15 and lane 31.
@@ -44,6 +44,31 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sbuf, 
 }
 
 
+// Two exclusive scans across the block in one pass (one pair of barriers).
+template <int TPB>
+__device__ __forceinline__ void block_excl_scan2(uint32_t v0, uint32_t v1, uint32_t (*sbuf2)[2], uint32_t* pre0,
+                                                 uint32_t* pre1, uint32_t* tot0, uint32_t* tot1) {
+  constexpr int NW = TPB / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t inc0 = wave_incl_scan(v0), inc1 = wave_incl_scan(v1);
+  if (lane == 63) sbuf2[wv][0] = inc0, sbuf2[wv][1] = inc1;
+  __syncthreads();
+  uint32_t o0 = 0, o1 = 0, t0 = 0, t1 = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t x0 = sbuf2[w][0], x1 = sbuf2[w][1];
+    o0 += w < wv ? x0 : 0u;
+    o1 += w < wv ? x1 : 0u;
+    t0 += x0;
+    t1 += x1;
+  }
+  __syncthreads();
+  *pre0 = o0 + inc0 - v0;
+  *pre1 = o1 + inc1 - v1;
+  *tot0 = t0;
+  *tot1 = t1;
+}
+
 // Selects the k largest of the row's keys (key[c] = score_key of position
 // threadIdx.x * C + c, 0 = not a candidate) and writes their positions --
 // mapped through gsel when given -- ascending to out (k slots, -1 padded) and
@@ -56,27 +81,33 @@ __device__ __forceinline__ void select_core(uint32_t (&key)[C], int n, int k, co
   constexpr int BPT = HIST_BINS / TPB;      // histogram bins scanned per thread
   __shared__ uint32_t hist[HIST_BINS];
   __shared__ uint32_t sbuf[NW];
-  __shared__ uint32_t sred[NW][3];
+  __shared__ uint32_t sred[NW][5];
   __shared__ uint32_t sh_digit, sh_above, sh_cnt;
-  __shared__ uint32_t rk_key[RANK_MAX], rk_n, sh_tau, sh_need;
+  __shared__ __align__(16) uint32_t rk_key[RANK_MAX];
+  __shared__ uint32_t rk_n, sh_tau, sh_need;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int i0 = t * C;
   if (t == 0) rk_n = 0;
-  (void)n;
+  // a thread's C keys lie in one 64-wide slice (C divides 64), so its group id
+  // (two-level selection) is one load, issued before the passes
+  static_assert(64 % C == 0, "a thread's keys must share one group");
+  const int gid = (gsel != nullptr && i0 < n) ? gsel[(size_t)row * n_gsel + i0 / 64] : 0;
 
   bool all = false;               // every candidate is kept (block-uniform)
   bool ranked = false;            // tau and its tie count are in sh_tau, sh_need
   uint32_t prefix = 0, kleft = (uint32_t)k;
   int pos = 32;
   if constexpr (RANGE) {
-    // candidate count and key range of the row
-    uint32_t kmin = 0xffffffffu, kmax = 0u, nv = 0;
+    // candidate count and key range of the row, and the same over the
+    // candidates scoring >= 0 (keys >= 0x80000000)
+    uint32_t kmin = 0xffffffffu, kmax = 0u, nv = 0, kmin_nn = 0xffffffffu, n_nn = 0;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       if (key[c]) {
         kmin = min(kmin, key[c]);
         kmax = max(kmax, key[c]);
         ++nv;
+        if (key[c] >= 0x80000000u) kmin_nn = min(kmin_nn, key[c]), ++n_nn;
       }
     }
 #pragma unroll
@@ -84,21 +115,31 @@ __device__ __forceinline__ void select_core(uint32_t (&key)[C], int n, int k, co
       kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
       kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
       nv += (uint32_t)__shfl_xor((int)nv, o, 64);
+      kmin_nn = min(kmin_nn, (uint32_t)__shfl_xor((int)kmin_nn, o, 64));
+      n_nn += (uint32_t)__shfl_xor((int)n_nn, o, 64);
     }
-    if (lane == 0) sred[wv][0] = kmin, sred[wv][1] = kmax, sred[wv][2] = nv;
+    if (lane == 0) sred[wv][0] = kmin, sred[wv][1] = kmax, sred[wv][2] = nv, sred[wv][3] = kmin_nn,
+                   sred[wv][4] = n_nn;
     __syncthreads();
-    kmin = 0xffffffffu, kmax = 0u, nv = 0;
+    kmin = 0xffffffffu, kmax = 0u, nv = 0, kmin_nn = 0xffffffffu, n_nn = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       kmin = min(kmin, sred[w][0]);
       kmax = max(kmax, sred[w][1]);
       nv += sred[w][2];
+      kmin_nn = min(kmin_nn, sred[w][3]);
+      n_nn += sred[w][4];
     }
     all = nv <= (uint32_t)k;
-    // from here on key[c] holds x = key - kmin + 1 for a candidate (no wrap:
-    // kmin >= 1), 0 for a non-candidate
+    // with at least k candidates scoring >= 0 the k-th lies among them, so the
+    // digits need only span their range: a row whose scores take both signs
+    // otherwise covers the whole key space, and its first pass is coarse.  Keys
+    // below the range can never be kept and count as non-candidates from here.
+    if (!all && n_nn >= (uint32_t)k) kmin = kmin_nn;
+    // from here on key[c] holds x = key - kmin + 1 for a candidate at or above
+    // kmin (no wrap: kmin >= 1), 0 otherwise
 #pragma unroll
-    for (int c = 0; c < C; ++c) key[c] = key[c] ? key[c] - kmin + 1u : 0u;
+    for (int c = 0; c < C; ++c) key[c] = key[c] >= kmin ? key[c] - kmin + 1u : 0u;
     pos = all ? 0 : 32 - __clz(kmax - kmin + 1u);
   }
 
@@ -109,6 +150,7 @@ __device__ __forceinline__ void select_core(uint32_t (&key)[C], int n, int k, co
     const int nb = 1 << (pos - sh);
     const uint32_t hmask = pos >= 32 ? 0u : (~0u << pos);   // bits already decided
     for (int i = t; i < nb; i += TPB) hist[i] = 0;
+    for (int i = t; i < (int)RANK_MAX; i += TPB) rk_key[i] = 0;   // the rank step reads 4 at a time
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -153,16 +195,34 @@ __device__ __forceinline__ void select_core(uint32_t (&key)[C], int n, int k, co
         if (x && (x & m2) == prefix) rk_key[atomicAdd(&rk_n, 1u)] = x;
       }
       __syncthreads();
-      if (wv == 0) {
-        const uint32_t cnt = rk_n;
-        const uint32_t kj = (uint32_t)lane < cnt ? rk_key[lane] : 0u;
-        uint32_t gt = 0, ge = 0;
-        for (uint32_t i = 0; i < cnt; ++i) {
-          const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)kj, (int)i);
-          gt += ki > kj;
-          ge += ki >= kj;
+      const uint32_t cnt = rk_n;
+      if (cnt <= 64) {
+        // one wave: lane j holds key j and reads the others from its neighbours
+        if (wv == 0) {
+          const uint32_t kj = (uint32_t)lane < cnt ? rk_key[lane] : 0u;
+          uint32_t gt = 0, ge = 0;
+          for (uint32_t i = 0; i < cnt; ++i) {
+            const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)kj, (int)i);
+            gt += ki > kj;
+            ge += ki >= kj;
+          }
+          if ((uint32_t)lane < cnt && gt < kleft && kleft <= ge) sh_tau = kj, sh_need = kleft - gt;
         }
-        if ((uint32_t)lane < cnt && gt < kleft && kleft <= ge) sh_tau = kj, sh_need = kleft - gt;
+      } else {
+        // thread t ranks key t of the bin against all of them (4-key LDS reads
+        // every thread makes at the same address); equal keys publish the same
+        // tau and count
+        if ((uint32_t)t < cnt) {
+          const uint32_t kj = rk_key[t];
+          uint32_t gt = 0, ge = 0;
+          const uint4* rk4 = reinterpret_cast<const uint4*>(rk_key);
+          for (uint32_t i = 0; i < (cnt + 3) / 4; ++i) {
+            const uint4 v = rk4[i];          // slots past cnt hold 0: never counted
+            gt += (v.x > kj) + (v.y > kj) + (v.z > kj) + (v.w > kj);
+            ge += (v.x >= kj) + (v.y >= kj) + (v.z >= kj) + (v.w >= kj);
+          }
+          if (gt < kleft && kleft <= ge) sh_tau = kj, sh_need = kleft - gt;
+        }
       }
       __syncthreads();
       ranked = true;
@@ -209,9 +269,9 @@ __device__ __forceinline__ void select_core(uint32_t (&key)[C], int n, int k, co
     gt += key[c] > tau;
     eq += key[c] == tau;
   }
-  uint32_t tot_gt, tot_eq;
-  const uint32_t gt_pre = block_excl_scan<TPB>(gt, sbuf, &tot_gt);
-  const uint32_t eq_pre = block_excl_scan<TPB>(eq, sbuf, &tot_eq);
+  __shared__ uint32_t sbuf2[NW][2];
+  uint32_t tot_gt, tot_eq, gt_pre, eq_pre;
+  block_excl_scan2<TPB>(gt, eq, sbuf2, &gt_pre, &eq_pre, &tot_gt, &tot_eq);
   uint32_t pos_out = gt_pre + min(eq_pre, need_eq);
   uint32_t eq_seen = eq_pre;
 #pragma unroll
@@ -223,7 +283,7 @@ __device__ __forceinline__ void select_core(uint32_t (&key)[C], int n, int k, co
     }
     if (sel) {
       const int i = i0 + c;
-      const int id = gsel ? gsel[(size_t)row * n_gsel + i / 64] * 64 + (i & 63) : i;
+      const int id = gsel ? gid * 64 + (i & 63) : i;
       out[pos_out++] = id;
     }
   }

@@ -152,7 +152,9 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   n_items = n_items < 0 ? 0 : (n_items > p.top_k ? p.top_k : n_items);
   const int t_pos = p.q_pos ? p.q_pos[row] : 0;
   const int n_tiles = (n_items + 3) / 4;
-  const int tps = (n_tiles + p.splits - 1) / p.splits;
+  // splits partition the row's top_k slots, not its count, so the first block
+  // ids are requested before the count arrives; the count only ends the loop
+  const int tps = ((p.top_k + 3) / 4 + p.splits - 1) / p.splits;
   const int t_begin = split * tps;
   const int t_end = min(n_tiles, t_begin + tps);
   const int n_ent = p.n_entries[b];
@@ -200,8 +202,8 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   // FP6 form: three E2M3 terms per 32-dim block.  Lane (head, hh), k-step s:
   // FP6 value k = dim 128dq + 64s + 32hh + k.  Each lane's 32 values are one
   // block of the scaled MFMA with its own E8M0 scale: every term rounds (to
-  // nearest even) what the earlier terms left, at the scale of its own largest
-  // value, which carries each value to within 2^-11.7 of the block's largest.
+  // nearest even) what the earlier terms left, each at a scale 2^4 finer than
+  // the last, which carries each value to within 2^-11.9 of the block's largest.
   // The scaled MFMA sums its 64 products to about 15 bits below the largest
   // one, so a query block whose values spread far below its largest (fewer than
   // half of them within 2^5 of it: an outlier channel over a bulk of small
@@ -234,39 +236,41 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
           x[8 * u + 2 * k + 1] = __uint_as_float(wv[k] & 0xFFFF0000u);
         }
       }
-      {
-        int emax = 0, near = 0;
-#pragma unroll
-        for (int k = 0; k < 32; ++k) emax = max(emax, (int)((__float_as_uint(x[k]) >> 23) & 0xFFu));
-#pragma unroll
-        for (int k = 0; k < 32; ++k) {
-          const int ek = (int)((__float_as_uint(x[k]) >> 23) & 0xFFu);
-          near += (ek != 0 && ek + 5 >= emax) ? 1 : 0;
-        }
-        wide |= emax != 0 && near < 16;
-      }
-      // y0[i], y1[i] = values 2i, 2i + 1 of the block, relative to 2^etot
+      // y0[i], y1[i] = values 2i, 2i + 1 of the block
       floatx16 y0, y1;
 #pragma unroll
       for (int i2 = 0; i2 < 16; ++i2) y0[i2] = x[2 * i2], y1[i2] = x[2 * i2 + 1];
-      int etot = 0;
+      float mx = 0.f;
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) mx = fmaxf(mx, fmaxf(fabsf(y0[i2]), fabsf(y1[i2])));
+      {
+        // values within 2^5 of the largest (same binade-or-above of 2^(e(mx) - 5))
+        const uint32_t em = __float_as_uint(mx) >> 23;
+        if (em > 5) {
+          const float thr = __uint_as_float((em - 5) << 23);
+          int near = 0;
+#pragma unroll
+          for (int k = 0; k < 32; ++k) near += fabsf(x[k]) >= thr ? 1 : 0;
+          wide |= near < 16;
+        }
+      }
+      // term scales 2^e0, 2^(e0 - 4), 2^(e0 - 8): the first puts the largest
+      // |value| in (3.75, 7.5]; E2M3 rounding leaves at most 0.25 of a term's
+      // scale, which the next term (2^4 finer) holds below 4, so no term
+      // saturates and the last leaves at most 2^(e0 - 10) <= 2^-11.9 of the
+      // largest.  The conversions take the scale (dividing, and multiplying back).
+      const int e0 = max(fp6_block_exp(mx, -126), -126);
+      const int ex[3] = {e0, max(e0 - 4, -126), max(e0 - 8, -126)};
 #pragma unroll
       for (int term = 0; term < 3; ++term) {
-        float mx = 0.f;
-#pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) mx = fmaxf(mx, fmaxf(fabsf(y0[i2]), fabsf(y1[i2])));
-        const int e = fp6_block_exp(mx, -127 - etot);
-        const float f = ldexpf(1.f, -e);
-#pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) y0[i2] *= f, y1[i2] *= f;     // a power of two
-        etot += e;
-        const int6v c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(y0, y1, 1.f);
+        const float sc = __uint_as_float((uint32_t)(127 + ex[term]) << 23);
+        const int6v c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(y0, y1, sc);
         qt[term][s] = int32x8{c[0], c[1], c[2], c[3], c[4], c[5], 0, 0};
-        const uint32_t sbyte = (uint32_t)(127 + etot);
+        const uint32_t sbyte = (uint32_t)(127 + ex[term]);
         if (term < 2) qsb |= sbyte << (8 * (2 * term + s));
         else qsb2 |= sbyte << (8 * s);
         if (term < 2) {
-          const floatx32 d = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, 1.f);
+          const floatx32 d = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, sc);
 #pragma unroll
           for (int i2 = 0; i2 < 16; ++i2) y0[i2] -= d[2 * i2], y1[i2] -= d[2 * i2 + 1];   // exact
         }

@@ -13,8 +13,11 @@
 // over the range the row's scores actually occupy (a fixed top-11-bit digit
 // puts a typical row into a handful of bins, and the LDS atomics on those few
 // bins serialise).  Each pass fixes up to 11 more bits of the K-th largest
-// key; once the bin holding it has at most 64 keys, those keys go to LDS and
-// one wave ranks them directly instead of running further passes.  A larger
+// key; once the bin holding it has at most 1024 keys, those keys go to LDS and
+// are ranked directly (one wave for up to 64, else every thread takes its share
+// of the bin and counts the keys above it) instead of running further passes:
+// rows whose scores span both signs cover the whole 32-bit key range, where
+// the first 2048-bin pass leaves a few hundred keys with the K-th.  A larger
 // bin's own key range places the next pass's digits (skipping the bits all its
 // keys share), and a bin of equal keys ends the search (planted blocks of equal
 // score pile up there).  Then a block-wide scan compacts the ids with key >
@@ -37,17 +40,24 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ sco
   const float* s = scores + (size_t)row * n;
   const int i0 = t * C;
 
+  // one decision per thread, so a full thread's vector loads are all in flight
+  // before the first is used (a per-chunk branch waits on each in turn)
   uint32_t key[C];
+  if (vec && i0 + C <= n) {
+    float4 v[C / 4];
 #pragma unroll
-  for (int c = 0; c < C; c += 4) {
-    if (vec && i0 + c + 3 < n) {
-      const float4 v = *reinterpret_cast<const float4*>(s + i0 + c);
-      key[c] = score_key(v.x), key[c + 1] = score_key(v.y);
-      key[c + 2] = score_key(v.z), key[c + 3] = score_key(v.w);
-    } else {
+    for (int c = 0; c < C / 4; ++c) v[c] = reinterpret_cast<const float4*>(s + i0)[c];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) key[c + j] = i0 + c + j < n ? score_key(s[i0 + c + j]) : 0u;
+    for (int c = 0; c < C / 4; ++c) {
+      key[4 * c] = score_key(v[c].x), key[4 * c + 1] = score_key(v[c].y);
+      key[4 * c + 2] = score_key(v[c].z), key[4 * c + 3] = score_key(v[c].w);
     }
+  } else {
+    float v[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) v[c] = i0 + c < n ? s[i0 + c] : -__builtin_inff();
+#pragma unroll
+    for (int c = 0; c < C; ++c) key[c] = score_key(v[c]);
   }
 
   sel::select_core<TPB, C, RANGE>(key, n, k, gsel, n_gsel, row, idx + (size_t)row * k, count + row);
