@@ -26,6 +26,7 @@ inline int launch_status(int rc) { return rc == 0 ? CSA2_OK : CSA2_ERR_LAUNCH; }
 // Index/top-K workspace pieces.
 struct IndexWs {
   size_t scores;      // fp32 [rows][n_score]
+  size_t gscore;      // fp32 [rows][cap / 512]
   size_t gsel;        // int32 [rows][top_groups]
   size_t gcount;      // int32 [rows]
   size_t total;
@@ -38,6 +39,7 @@ IndexWs index_ws_layout(int B, int Q, int cap, int top_groups) {
   size_t off = 0;
   l.scores = off; off += align_up(rows * n_score * sizeof(float));
   if (top_groups > 0) {
+    l.gscore = off; off += align_up(rows * ((size_t)cap / 512) * sizeof(float));
     l.gsel = off; off += align_up(rows * (size_t)top_groups * sizeof(int32_t));
     l.gcount = off; off += align_up(rows * sizeof(int32_t));
   }
@@ -160,7 +162,9 @@ int csa2::index_topk_run(const uint16_t* q_idx, const float* w, const KeyCache& 
   if ((size_t)top_groups * CSA2_GROUP_BLOCKS > 65536) return CSA2_ERR_UNSUPPORTED;
   int32_t* gsel = reinterpret_cast<int32_t*>(base + l.gsel);
   int32_t* gcount = reinterpret_cast<int32_t*>(base + l.gcount);
-  int rc = launch_coarse_select(q_idx, w, group_sum, n_entries, B, Q, Hi, cap, top_groups, gsel, gcount, st);
+  float* gscore = reinterpret_cast<float*>(base + l.gscore);
+  int rc = launch_coarse_scores(q_idx, w, group_sum, n_entries, B, Q, Hi, cap, gscore, st);
+  if (!rc) rc = launch_topk(gscore, rows, G, top_groups, nullptr, 0, gsel, gcount, st);
   if (!rc) rc = launch_index_scores(q_idx, w, keys, n_entries, nullptr, B, Q, Hi, cap, gsel, top_groups,
                                     scores, st);
   if (!rc) rc = launch_topk(scores, rows, top_groups * CSA2_GROUP_BLOCKS, top_k, gsel, top_groups,

@@ -48,7 +48,8 @@ int launch_window(const AttnParams& p, hipStream_t stream) {
 // ---- combine -----------------------------------------------------------
 // Log-sum-exp merge of the split-K partials (and an optional fp32 extra
 // branch) of one (row, head): wave 0 turns the partials' lse and exponents into
-// weights in LDS, then every thread streams 4 of the 512 dims over the splits.
+// weights in LDS, then every thread streams 4 of the 512 dims over the splits,
+// 16 splits in flight at a time.
 constexpr int MAX_COMBINE_SPLITS = 128;
 
 __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ o16,
@@ -86,22 +87,30 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
       L_sh = L;
     }
   }
-  __syncthreads();
   typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
   const uint2* src = reinterpret_cast<const uint2*>(o16 + part0 * D) + t;
   const size_t stride = (size_t)H * D / 4;                       // one split, in uint2
+  // 16 splits' loads in flight per thread, the first 16 requested before the
+  // weights are ready (the partials do not depend on them)
+  constexpr int PF = 16;
+  uint2 buf[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) buf[i] = i < splits ? src[(size_t)i * stride] : make_uint2(0u, 0u);
+  __syncthreads();
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto add = [&](uint2 v, float wv) {
-    const floatx4 f = __builtin_convertvector(__builtin_bit_cast(halfx4, v), floatx4);
-    acc.x += wv * f[0]; acc.y += wv * f[1]; acc.z += wv * f[2]; acc.w += wv * f[3];
-  };
-  int s = 0;
-  for (; s + 4 <= splits; s += 4) {
-    const uint2 v0 = src[(s + 0) * stride], v1 = src[(s + 1) * stride];
-    const uint2 v2 = src[(s + 2) * stride], v3 = src[(s + 3) * stride];
-    add(v0, wts[s]); add(v1, wts[s + 1]); add(v2, wts[s + 2]); add(v3, wts[s + 3]);
+  for (int s0 = 0; s0 < splits; s0 += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      if (s0 + i < splits) {
+        const floatx4 f = __builtin_convertvector(__builtin_bit_cast(halfx4, buf[i]), floatx4);
+        const float wv = wts[s0 + i];
+        acc.x += wv * f[0]; acc.y += wv * f[1]; acc.z += wv * f[2]; acc.w += wv * f[3];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      if (s0 + PF + i < splits) buf[i] = src[(size_t)(s0 + PF + i) * stride];
   }
-  for (; s < splits; ++s) add(src[s * stride], wts[s]);
   if (o_ext) {
     const float we = wts[splits];
     if (we != 0.f) {

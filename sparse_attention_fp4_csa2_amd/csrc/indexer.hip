@@ -283,50 +283,70 @@ __global__ __launch_bounds__(256) void index_rows_kernel(
   if (e < e_end) score(e, k0);
 }
 
-// Two-level stage, coarse part, in one launch: one 1024-thread workgroup per
-// query row, thread g = group g.  Each thread requests its group's 64 summed
-// key dims at once (one round of memory latency for the whole row) and forms
-// sum_h w_h max(0, q_h . sum / count) (count = the group's present entries).
-// The row's indexer query is the same for every thread: it is read through
-// the scalar unit (a uniform address in the constant address space), so each
-// query value is one scalar operand of the threads' FMAs instead of a vector
-// read per thread.  The radix select of the top-K kernels then keeps the best
-// top_groups groups (ascending ids, -1 padded, with their count), with digits
-// relative to the row's score range (group scores share a few exponents, so
-// fixed top-bit digits would take several passes).  G = cap / 512 <= 1024 (cap / 8 <= 65536).
-constexpr int COARSE_TPB = 1024;
-typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+// Two-level stage, coarse scores: a [Hi x 64] x [64 x G] contraction per query
+// row on v_mfma_f32_16x16x32_bf16, as the fine indexer's: A = the row's
+// indexer query (heads padded to 16), B = 16 group means, each mean (fp32 sum
+// / present count) split into bf16 hi + lo (16 significant bits between them),
+// so a 16-group tile takes 4 MFMAs.  The epilogue applies ReLU and the head
+// weights and sums the heads; groups with no entry score -inf.  A row's group
+// sums (G x 256 B, 256 KB at G = 1024) are spread over G / 64 workgroups of
+// 64 groups (one tile per wave): one workgroup per row would stream them
+// through a single CU.  grid: (ceil(G / 64), rows).
+constexpr int COARSE_GROUPS_WG = 64;
 
-__global__ __launch_bounds__(COARSE_TPB) void coarse_select_kernel(
+__global__ __launch_bounds__(256) void coarse_scores_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const float* __restrict__ group_sum,
-    const int32_t* __restrict__ n_entries, int Q, int Hi, int cap, int top_groups, int32_t* __restrict__ gsel,
-    int32_t* __restrict__ gcount) {
-  const int row = blockIdx.x, b = row / Q;
+    const int32_t* __restrict__ n_entries, int Q, int Hi, int cap, float* __restrict__ gscore) {
+  const int row = blockIdx.y, b = row / Q;
   const int G = cap / GROUP_ENTRIES;
-  const int ne = min(n_entries[b], cap);
-  const int g = threadIdx.x;
-  const int cnt = g < G ? min(GROUP_ENTRIES, ne - g * GROUP_ENTRIES) : 0;
-  float4 m4[DI / 4];
-  const float4* gs = reinterpret_cast<const float4*>(group_sum + ((size_t)b * G + min(g, G - 1)) * DI);
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int n = lane & 15;            // group within the tile / head row of A
+  const int kg = lane >> 4;           // k-group: dims [8kg, 8kg + 8) of each 32-dim k-step
+  const int g = blockIdx.x * COARSE_GROUPS_WG + wave * 16 + n;
+  // this lane's group-sum dims 32ks + 8kg + [0, 8), ks = 0, 1 (all requested first)
+  float4 gs[2][2];
+  {
+    const float4* src = reinterpret_cast<const float4*>(group_sum + ((size_t)b * G + min(g, G - 1)) * DI + 8 * kg);
 #pragma unroll
-  for (int d4 = 0; d4 < DI / 4; ++d4) m4[d4] = gs[d4];
-  const const_u32_ptr qrow = (const_u32_ptr)(const void*)(q_idx + (size_t)row * Hi * DI);
-  const const_u32_ptr wrow = (const_u32_ptr)(const void*)(w + (size_t)row * Hi);
-  const float inv = cnt > 0 ? 1.f / (float)cnt : 0.f;
-  float s = 0.f;
-  for (int h = 0; h < Hi; ++h) {
-    float dot = 0.f;
-#pragma unroll
-    for (int d4 = 0; d4 < DI / 4; ++d4) {
-      const uint32_t q01 = qrow[h * (DI / 2) + 2 * d4], q23 = qrow[h * (DI / 2) + 2 * d4 + 1];
-      dot += __uint_as_float(q01 << 16) * m4[d4].x + __uint_as_float(q01 & 0xFFFF0000u) * m4[d4].y +
-             __uint_as_float(q23 << 16) * m4[d4].z + __uint_as_float(q23 & 0xFFFF0000u) * m4[d4].w;
-    }
-    s += __uint_as_float(wrow[h]) * fmaxf(dot * inv, 0.f);
+    for (int ks = 0; ks < 2; ++ks) gs[ks][0] = src[8 * ks], gs[ks][1] = src[8 * ks + 1];
   }
-  uint32_t key[1] = {cnt > 0 ? score_key(s) : 0u};
-  sel::select_core<COARSE_TPB, 1, true>(key, G, top_groups, nullptr, 0, row, gsel + (size_t)row * top_groups,
-                                         gcount + row);
+  // A fragments: head n (< Hi), dims 32ks + 8kg + [0, 8)
+  uint4 qa[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    qa[ks] = n < Hi ? *reinterpret_cast<const uint4*>(q_idx + ((size_t)row * Hi + n) * DI + 32 * ks + 8 * kg)
+                    : make_uint4(0, 0, 0, 0);
+  float wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wv[i] = 4 * kg + i < Hi ? w[(size_t)row * Hi + 4 * kg + i] : 0.f;
+  const int ne = min(n_entries[b], cap);
+  const int cnt = g < G ? min(GROUP_ENTRIES, ne - g * GROUP_ENTRIES) : 0;
+  const float inv = cnt > 0 ? 1.f / (float)cnt : 0.f;
+
+  floatx4 acc = floatx4{};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const float v[8] = {gs[ks][0].x * inv, gs[ks][0].y * inv, gs[ks][0].z * inv, gs[ks][0].w * inv,
+                        gs[ks][1].x * inv, gs[ks][1].y * inv, gs[ks][1].z * inv, gs[ks][1].w * inv};
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t h0 = f32_to_bf16_rne(v[2 * k]), h1 = f32_to_bf16_rne(v[2 * k + 1]);
+      const uint32_t l0 = f32_to_bf16_rne(v[2 * k] - __uint_as_float(h0 << 16));
+      const uint32_t l1 = f32_to_bf16_rne(v[2 * k + 1] - __uint_as_float(h1 << 16));
+      hi[k] = h0 | (h1 << 16);
+      lo[k] = l0 | (l1 << 16);
+    }
+    acc = mfma16(qa[ks], make_uint4(hi[0], hi[1], hi[2], hi[3]), acc);
+    acc = mfma16(qa[ks], make_uint4(lo[0], lo[1], lo[2], lo[3]), acc);
+  }
+  // acc[i]: head 4kg + i, group n
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part += wv[i] * fmaxf(acc[i], 0.f);
+  part += __shfl_xor(part, 16, 64);
+  part += __shfl_xor(part, 32, 64);
+  if (kg == 0 && g < G) gscore[(size_t)row * G + g] = cnt > 0 ? part : -__builtin_inff();
 }
 
 template <bool K8>
@@ -365,12 +385,12 @@ int launch_index_scores(const uint16_t* q_idx, const float* w, const KeyCache& k
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int launch_coarse_select(const uint16_t* q_idx, const float* w, const float* group_sum,
-                         const int32_t* n_entries, int B, int Q, int Hi, int cap, int top_groups, int32_t* gsel,
-                         int32_t* gcount, hipStream_t stream) {
-  if (cap / GROUP_ENTRIES > COARSE_TPB) return -4;
-  coarse_select_kernel<<<B * Q, COARSE_TPB, 0, stream>>>(q_idx, w, group_sum, n_entries, Q, Hi, cap, top_groups,
-                                                         gsel, gcount);
+int launch_coarse_scores(const uint16_t* q_idx, const float* w, const float* group_sum,
+                         const int32_t* n_entries, int B, int Q, int Hi, int cap, float* gscore, hipStream_t stream) {
+  const int G = cap / GROUP_ENTRIES;
+  if (G < 1) return -4;
+  coarse_scores_kernel<<<dim3((G + COARSE_GROUPS_WG - 1) / COARSE_GROUPS_WG, B * Q), 256, 0, stream>>>(
+      q_idx, w, group_sum, n_entries, Q, Hi, cap, gscore);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

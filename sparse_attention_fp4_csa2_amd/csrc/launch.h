@@ -38,12 +38,10 @@ int launch_index_scores(const uint16_t* q_idx, const float* w, const KeyCache& k
                         int cap, const int32_t* gsel, int n_groups_sel, float* scores,
                         hipStream_t stream);
 
-// Coarse stage of the two-level indexer in one launch: group scores from the
-// group sums and the top_groups best groups per row -> gsel [rows][top_groups]
-// (ascending, -1 padded), gcount [rows].  cap / 512 <= 1024.
-int launch_coarse_select(const uint16_t* q_idx, const float* w, const float* group_sum,
-                         const int32_t* n_entries, int B, int Q, int Hi, int cap, int top_groups, int32_t* gsel,
-                         int32_t* gcount, hipStream_t stream);
+// Coarse scores of the two-level indexer: the score of every group from its
+// group sums -> gscore [rows][cap / 512] (-inf for groups with no entry).
+int launch_coarse_scores(const uint16_t* q_idx, const float* w, const float* group_sum,
+                         const int32_t* n_entries, int B, int Q, int Hi, int cap, float* gscore, hipStream_t stream);
 
 // Top-k per row of scores [rows][n] -> idx [rows][k] ascending, -1 padded, count [rows].
 // With gsel != nullptr, position p maps to block gsel[row][p / 64] * 64 + p % 64.

@@ -105,7 +105,7 @@ def test_workspace_sizes_are_pure_and_monotone(lib):
     a = lib.csa2_index_topk_ws(32, 1, 32768, 0)
     assert a >= 32 * 4096 * 4
     b = lib.csa2_index_topk_ws(8, 1, 524288, 256)
-    # block scores over the kept groups, the kept group ids and their counts
-    assert b >= 8 * 256 * 64 * 4 + 8 * 256 * 4 + 8 * 4
+    # block scores over the kept groups, the group scores, the kept group ids and their counts
+    assert b >= 8 * 256 * 64 * 4 + 8 * 1024 * 4 + 8 * 256 * 4 + 8 * 4
     assert lib.csa2_swa_merge_ws(32, 1, 64, 512) >= lib.csa2_swa_merge_ws(1, 1, 64, 512)
     assert lib.csa2_index_topk_ws(0, 1, 8, 0) == 0
