@@ -47,14 +47,15 @@ METRIC = "sparse-attn decode queries/s and TB/s FP4 KV read; % of HBM/MFMA roofl
 PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 RECORD = 2176
-# HBM bytes per csa2_sparse_attn call from rocprofv3 FETCH_SIZE / WRITE_SIZE
-# counter runs, with the hash of the kernel source they were taken on
+# HBM bytes per csa2_attend_layer call (attend_kernel + its combine) from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs, with the hash of the kernel
+# sources they were taken on
 KERNEL_SRCS = [os.path.join(ROOT, "sparse_attention_fp4_csa2_amd", "csrc", f)
-               for f in ("sparse_fp4.hip", "attention.hip")]
+               for f in ("sparse_fp4.hip", "attention.hip", "window_body.h", "device.h")]
 
 
 def traffic_file(config):
-    return os.path.join(ROOT, "profiles", f"traffic_sparse_attn_{config}.json")
+    return os.path.join(ROOT, "profiles", f"traffic_attend_layer_{config}.json")
 
 
 def parse(argv=None):
@@ -82,6 +83,14 @@ def parse(argv=None):
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain fp32 copy kernel over this many bytes "
                          "(the calibration point for rocprofv3 FETCH_SIZE / WRITE_SIZE runs)")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="no GPU work: turn rocprofv3 CSV output into a profile summary on stdout. "
+                         "'trace KERNEL_TRACE_CSV BENCH_JSON' (per-kernel durations, markdown), "
+                         "'traffic FETCH_CSV WRITE_CSV COPY_BYTES' (HBM bytes per csa2_attend_layer "
+                         "call, JSON), 'counters COUNTER_CSV' (SQ counters per kernel, markdown); "
+                         "--config names the workload, --command the commands that made the input")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --summarize: a command that produced the input (recorded verbatim)")
     return ap.parse_args(argv)
 
 
@@ -473,6 +482,8 @@ def measure(name, args):
 
 def main():
     args = parse()
+    if args.summarize:
+        sys.exit(summarize(args))
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by sequence/row with no exchange; see the design notes).",
@@ -625,6 +636,180 @@ def stored_traffic(config):
     if rec.get("kernel_sources_sha256") != digest:
         return None
     return rec.get("bytes_per_call")
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 output -> the profile summaries kept with the sources
+
+_CALL_OF_COMBINE = {"attend_kernel": "csa2_attend_layer", "sparse_fp4_kernel": "csa2_sparse_attn",
+                    "window_kernel": "csa2_swa_merge"}
+
+
+def _kernel_label(name, prev_csa2):
+    """Short label of a dispatch: csa2 kernels without namespace and argument
+    list, the bf16- and MXFP8-key indexers told apart, combine_kernel named by
+    the call it closes (the csa2 kernel dispatched before it)."""
+    base = name.split("(")[0].replace("void ", "").strip()
+    if not base.startswith("csa2::"):
+        return None
+    base = base[len("csa2::"):]
+    if base.startswith("index_scores_kernel") or base.startswith("index_rows_kernel"):
+        base += " (MXFP8 keys)" if base.rstrip(">").endswith("true") else " (bf16 keys)"
+    if base == "combine_kernel":
+        base += f" ({_CALL_OF_COMBINE.get(prev_csa2, 'csa2_attend_layer')})"
+    return base
+
+
+def _labelled(rows):
+    """rows: (name, start_ns, end_ns, extra) sorted by start -> (label, cold, dur_us, extra).
+    A dispatch is cold when it runs in the same back-to-back burst as a
+    preceding 1 GiB flush read (no idle gap above 15 us since it)."""
+    out, prev_csa2, cold, last_end = [], None, False, None
+    for name, st, en, extra in rows:
+        if last_end is not None and st - last_end > 15000:
+            cold = False
+        last_end = en if last_end is None else max(last_end, en)
+        if "reduce_kernel" in name:
+            cold = True
+            continue
+        lab = _kernel_label(name, prev_csa2)
+        if lab is None:
+            continue
+        prev_csa2 = name.split("(")[0].replace("void ", "").strip()[len("csa2::"):]
+        out.append((lab, cold, (en - st) / 1000.0, extra))
+    return out
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _commands_block(args):
+    return "\n".join(args.command) if args.command else "(not recorded)"
+
+
+def summarize(args):
+    from synth import CONFIGS
+    kind, inputs = args.summarize[0], args.summarize[1:]
+    cfg_desc = workload_config(CONFIGS[args.config], None, args.index_keys)["workload"]
+    if kind == "trace":
+        rows = _read_csv(inputs[0])
+        disp = sorted(((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"]), None)
+                       for r in rows), key=lambda x: x[1])
+        lab = _labelled(disp)
+        bench = json.loads(open(inputs[1]).read().strip().splitlines()[-1]) if len(inputs) > 1 else None
+        by = {}
+        for k, cold, d, _ in lab:
+            by.setdefault(k, {"cold": [], "warm": []})["cold" if cold else "warm"].append(d)
+        lines = [f"# Kernel trace: {cfg_desc}", "", "Commands (repository root on the GPU host as `$REPO`):",
+                 "", "```", _commands_block(args), "```", "",
+                 "Per-dispatch durations from the kernel-trace CSV, split into cold dispatches (in the "
+                 "back-to-back burst after a 1 GiB scratch read that evicts L2 and the last-level cache) "
+                 "and warm ones (the rest: settle, warm-up and back-to-back loops).  `combine_kernel` is "
+                 "named by the call it closes; torch's own kernels are left out.", "",
+                 "| kernel | warm n | warm median µs | warm mean µs | cold n | cold mean µs | min µs |",
+                 "|---|---|---|---|---|---|---|"]
+        order = sorted(by.items(), key=lambda kv: -sum(kv[1]["warm"] + kv[1]["cold"]))
+        for k, v in order:
+            w, c = v["warm"], v["cold"]
+            fmt = lambda x: f"{x:.2f}" if x is not None else "-"   # noqa: E731
+            lines.append(f"| {k} | {len(w)} | {fmt(float(np.median(w)) if w else None)} | "
+                         f"{fmt(float(np.mean(w)) if w else None)} | {len(c)} | "
+                         f"{fmt(float(np.mean(c)) if c else None)} | {min(w + c):.2f} |")
+        att = by.get("attend_kernel"), by.get("combine_kernel (csa2_attend_layer)")
+        if all(att) and bench is not None:
+            wm = float(np.median(att[0]["warm"])) + float(np.median(att[1]["warm"]))
+            cm = (float(np.mean(att[0]["cold"])) + float(np.mean(att[1]["cold"]))) if att[0]["cold"] and \
+                att[1]["cold"] else None
+            ev_w = bench.get("breakdown_ms", {}).get("attend_layer")
+            ev_c = bench.get("cold_breakdown_ms", {}).get("attend_layer")
+            lines += ["", "The roofline's unit, one `csa2_attend_layer` call = `attend_kernel` + its "
+                      "`combine_kernel`:", "",
+                      f"- warm: trace medians {wm:.2f} µs; the traced run's own HIP-event time per call "
+                      f"{ev_w * 1000:.2f} µs" if ev_w is not None else f"- warm: trace medians {wm:.2f} µs"]
+            if cm is not None:
+                lines.append(f"- cold: trace means {cm:.2f} µs; HIP events {ev_c * 1000:.2f} µs "
+                             "(the roofline's `achieved` divides by this one)" if ev_c is not None
+                             else f"- cold: trace means {cm:.2f} µs")
+        if bench is not None:
+            keep = {k: bench[k] for k in ("value", "unit", "ms_per_step", "warm_value", "warm_ms_per_step",
+                                          "cold_breakdown_ms", "breakdown_ms", "roofline") if k in bench}
+            lines += ["", "The traced bench.py run's line (profiling slows it; the figures above are from "
+                      "the trace itself):", "", "```", json.dumps(keep), "```"]
+        print("\n".join(lines))
+        return 0
+    if kind == "traffic":
+        copy_bytes = int(inputs[2])
+        per = {}
+        for counter, path in (("FETCH_SIZE", inputs[0]), ("WRITE_SIZE", inputs[1])):
+            rows = [r for r in _read_csv(path) if r["Counter_Name"] == counter]
+            disp = sorted(((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                            float(r["Counter_Value"])) for r in rows), key=lambda x: x[1])
+            vals = {}
+            for k, _, _, v in _labelled(disp):
+                vals.setdefault(k, []).append(v)
+            # the calibration copy: the largest MulFunctor dispatches (bench.py runs it 3 times)
+            muls = [float(r["Counter_Value"]) for r in rows if "MulFunctor" in r["Kernel_Name"]]
+            copy = [v for v in muls if v >= 0.5 * max(muls)] if muls else []
+            if not copy:
+                print(f"no calibration copy kernel in {path}", file=sys.stderr)
+                return 1
+            vals["copy"] = copy
+            per[counter] = {k: float(np.median(v)) for k, v in vals.items()}
+        f_fac = copy_bytes / 1024.0 / per["FETCH_SIZE"]["copy"]
+        w_fac = copy_bytes / 1024.0 / per["WRITE_SIZE"]["copy"]
+        call = ("attend_kernel", "combine_kernel (csa2_attend_layer)")
+        fetch = sum(per["FETCH_SIZE"][k] for k in call) * 1024 * f_fac
+        write = sum(per["WRITE_SIZE"][k] for k in call) * 1024 * w_fac
+        cfg = CONFIGS[args.config]
+        rec = {"kernel": "csa2_attend_layer call = attend_kernel + combine_kernel",
+               "workload": cfg_desc, "kernel_sources_sha256": kernel_digest(),
+               "bytes_per_call": int(round(fetch + write)), "fetch_bytes_per_call": int(round(fetch)),
+               "write_bytes_per_call": int(round(write)),
+               "selected_record_bytes_per_call": int(2176 * cfg.K * (cfg.B * cfg.Q)),
+               "median_KiB_per_dispatch": {c: {k: round(v, 1) for k, v in d.items()} for c, d in per.items()},
+               "calibration": {"copy_kernel": f"torch.mul(src, 1.0, out=dst) over {copy_bytes} bytes of fp32 "
+                                              f"(reads and writes {copy_bytes} bytes)",
+                               "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+               "commands": args.command}
+        print(json.dumps(rec, indent=1))
+        return 0
+    if kind == "counters":
+        rows = _read_csv(inputs[0])
+        by_disp = {}
+        for r in rows:
+            key = int(r["Dispatch_Id"])
+            d = by_disp.setdefault(key, {"name": r["Kernel_Name"], "st": int(r["Start_Timestamp"]),
+                                         "en": int(r["End_Timestamp"]), "c": {}})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        disp = sorted(((d["name"], d["st"], d["en"], d["c"]) for d in by_disp.values()), key=lambda x: x[1])
+        agg = {}
+        for k, _, _, c in _labelled(disp):
+            a = agg.setdefault(k, {"n": 0})
+            a["n"] += 1
+            for cn, v in c.items():
+                a[cn] = a.get(cn, 0.0) + v
+        names = sorted({cn for a in agg.values() for cn in a if cn != "n"})
+        lines = [f"# SQ counters: {cfg_desc}", "", "Commands (repository root on the GPU host as `$REPO`):",
+                 "", "```", _commands_block(args), "```", "",
+                 "Sums per dispatch, averaged over the dispatches of each kernel.  MFMA busy = "
+                 "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8): GRBM_GUI_ACTIVE sums the "
+                 "8 XCDs' busy clocks, so /8 is the kernel's duration in clocks.", "",
+                 "| kernel | n | MFMA busy | " + " | ".join(names) + " |",
+                 "|---|---|---|" + "---|" * len(names)]
+        for k, a in sorted(agg.items(), key=lambda kv: -kv[1].get("GRBM_GUI_ACTIVE", 0) * kv[1]["n"]):
+            n = a["n"]
+            busy = "-"
+            if a.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in a:
+                busy = f"{a['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024.0 * a['GRBM_GUI_ACTIVE'] / 8.0):.3f}"
+            lines.append(f"| {k} | {n} | {busy} | " + " | ".join(f"{a.get(c, 0.0) / n:.4g}" for c in names)
+                         + " |")
+        print("\n".join(lines))
+        return 0
+    print(f"unknown summary kind {kind}", file=sys.stderr)
+    return 2
 
 
 # ---------------------------------------------------------------------------

@@ -48,87 +48,119 @@ int launch_window(const AttnParams& p, hipStream_t stream) {
 // ---- combine -----------------------------------------------------------
 // Log-sum-exp merge of the split-K partials (and an optional fp32 extra
 // branch) of one (row, head): wave 0 turns the partials' lse and exponents into
-// weights in LDS, then every thread streams 4 of the 512 dims over the splits,
-// 16 splits in flight at a time.
+// weights in LDS while every wave already streams its share of the partials:
+// wave g takes splits g, g + 4, ..., each lane 8 of the 512 dims (16-byte
+// loads, 8 splits in flight); the four waves' sums meet in LDS and each thread
+// writes 2 dims.  512 dims x 33 splits of fp16 at 64 heads x 8 rows is 17 MB:
+// bandwidth-bound, so each CU needs many bytes in flight.
 constexpr int MAX_COMBINE_SPLITS = 128;
+constexpr int CMB_WAVES = 4;
+constexpr int CMB_PF = 8;
 
-__global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ o16,
-                                                      const int32_t* __restrict__ oexp,
-                                                      const float* __restrict__ lse_part,
-                                                      int splits, int H,
-                                                      const float* __restrict__ o_ext,
-                                                      const float* __restrict__ lse_ext,
-                                                      float* __restrict__ out,
-                                                      float* __restrict__ lse_out) {
+__global__ __launch_bounds__(64 * CMB_WAVES) void combine_kernel(const uint16_t* __restrict__ o16,
+                                                                 const int32_t* __restrict__ oexp,
+                                                                 const float* __restrict__ lse_part,
+                                                                 int splits, int H,
+                                                                 const float* __restrict__ o_ext,
+                                                                 const float* __restrict__ lse_ext,
+                                                                 float* __restrict__ out,
+                                                                 float* __restrict__ lse_out) {
   __shared__ float wts[MAX_COMBINE_SPLITS + 1];
   __shared__ float L_sh;
+  __shared__ __align__(16) float red[CMB_WAVES][D];
   const int h = blockIdx.x, row = blockIdx.y, t = threadIdx.x;
+  const int g = t >> 6, l = t & 63;
   const size_t rh = (size_t)row * H + h;
   const size_t part0 = (size_t)row * splits * H + h;              // split s at part0 + s * H
   const float* lp = lse_part + part0;
-  if (t < 64) {
-    const float le = (o_ext && t == 0) ? lse_ext[rh] : -__builtin_inff();
-    float m = le;
-    for (int s = t; s < splits; s += 64) m = fmaxf(m, lp[(size_t)s * H]);
+
+  // this wave's partials: splits g + 4i, lane dims [8l, 8l + 8); the first
+  // CMB_PF requested before the weights exist (they do not depend on them)
+  typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+  const uint4* src = reinterpret_cast<const uint4*>(o16 + part0 * D) + l;
+  const size_t stride = (size_t)CMB_WAVES * H * D / 8;           // 4 splits, in uint4
+  const int n_mine = g < splits ? (splits - g + CMB_WAVES - 1) / CMB_WAVES : 0;
+  src += (size_t)g * H * D / 8;
+  uint4 buf[CMB_PF];
+#pragma unroll
+  for (int i = 0; i < CMB_PF; ++i) buf[i] = i < n_mine ? src[(size_t)i * stride] : make_uint4(0u, 0u, 0u, 0u);
+
+  if (g == 0) {
+    // lane l holds splits l and l + 64 (splits <= 128): every load issued at once
+    float lv[2];
+    int ev[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int s = l + 64 * j;
+      lv[j] = s < splits ? lp[(size_t)s * H] : -__builtin_inff();
+      ev[j] = s < splits ? oexp[part0 + (size_t)s * H] : 0;
+    }
+    const float le = (o_ext && l == 0) ? lse_ext[rh] : -__builtin_inff();
+    float m = fmaxf(le, fmaxf(lv[0], lv[1]));
 #pragma unroll
     for (int k = 1; k < 64; k <<= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
     float sum = 0.f;
-    if (m != -__builtin_inff()) {
-      for (int s = t; s < splits; s += 64) sum += expf(lp[(size_t)s * H] - m);
-      if (t == 0 && o_ext) sum += expf(le - m);
-    }
+    if (m != -__builtin_inff()) sum = expf(lv[0] - m) + expf(lv[1] - m) + expf(le - m);
 #pragma unroll
     for (int k = 1; k < 64; k <<= 1) sum += __shfl_xor(sum, k, 64);
     const float L = m == -__builtin_inff() ? -__builtin_inff() : m + logf(sum);
-    for (int s = t; s < splits; s += 64)
-      wts[s] = L == -__builtin_inff() ? 0.f : ldexpf(expf(lp[(size_t)s * H] - L), oexp[part0 + (size_t)s * H]);
-    if (t == 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int s = l + 64 * j;
+      if (s < splits) wts[s] = L == -__builtin_inff() ? 0.f : ldexpf(expf(lv[j] - L), ev[j]);
+    }
+    if (l == 0) {
       wts[splits] = (o_ext && L != -__builtin_inff()) ? expf(le - L) : 0.f;
       L_sh = L;
     }
   }
-  typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
-  const uint2* src = reinterpret_cast<const uint2*>(o16 + part0 * D) + t;
-  const size_t stride = (size_t)H * D / 4;                       // one split, in uint2
-  // 16 splits' loads in flight per thread, the first 16 requested before the
-  // weights are ready (the partials do not depend on them)
-  constexpr int PF = 16;
-  uint2 buf[PF];
-#pragma unroll
-  for (int i = 0; i < PF; ++i) buf[i] = i < splits ? src[(size_t)i * stride] : make_uint2(0u, 0u);
   __syncthreads();
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < splits; s0 += PF) {
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < n_mine; i0 += CMB_PF) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      if (s0 + i < splits) {
-        const floatx4 f = __builtin_convertvector(__builtin_bit_cast(halfx4, buf[i]), floatx4);
-        const float wv = wts[s0 + i];
-        acc.x += wv * f[0]; acc.y += wv * f[1]; acc.z += wv * f[2]; acc.w += wv * f[3];
+    for (int i = 0; i < CMB_PF; ++i) {
+      if (i0 + i < n_mine) {
+        const float wv = wts[g + CMB_WAVES * (i0 + i)];
+        const halfx8 hv = __builtin_bit_cast(halfx8, buf[i]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] += wv * (float)hv[k];
       }
     }
 #pragma unroll
-    for (int i = 0; i < PF; ++i)
-      if (s0 + PF + i < splits) buf[i] = src[(size_t)(s0 + PF + i) * stride];
+    for (int i = 0; i < CMB_PF; ++i)
+      if (i0 + CMB_PF + i < n_mine) buf[i] = src[(size_t)(i0 + CMB_PF + i) * stride];
+  }
+  reinterpret_cast<float4*>(&red[g][8 * l])[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  reinterpret_cast<float4*>(&red[g][8 * l])[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  __syncthreads();
+
+  // thread t: dims 2t, 2t + 1
+  float2 o = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int w = 0; w < CMB_WAVES; ++w) {
+    const float2 v = reinterpret_cast<const float2*>(red[w])[t];
+    o.x += v.x; o.y += v.y;
   }
   if (o_ext) {
+    // o_ext may alias out: this thread reads exactly the dims it then writes
     const float we = wts[splits];
     if (we != 0.f) {
-      const float4 v = reinterpret_cast<const float4*>(o_ext + rh * D)[t];
-      acc.x += we * v.x; acc.y += we * v.y; acc.z += we * v.z; acc.w += we * v.w;
+      const float2 v = reinterpret_cast<const float2*>(o_ext + rh * D)[t];
+      o.x += we * v.x; o.y += we * v.y;
     }
   }
-  __syncthreads();   // o_ext may alias out: every read above precedes the writes below
-  reinterpret_cast<float4*>(out + rh * D)[t] = acc;
+  reinterpret_cast<float2*>(out + rh * D)[t] = o;
   if (t == 0) lse_out[rh] = L_sh;
 }
 
 int launch_combine(const uint16_t* o16, const int32_t* oexp, const float* lse_part, int rows,
                    int splits, int H, const float* o_ext, const float* lse_ext, float* out,
                    float* lse_out, hipStream_t stream) {
+  if (splits > MAX_COMBINE_SPLITS) return -4;
   dim3 grid(H, rows);
-  combine_kernel<<<grid, 128, 0, stream>>>(o16, oexp, lse_part, splits, H, o_ext, lse_ext, out,
-                                           lse_out);
+  combine_kernel<<<grid, 64 * CMB_WAVES, 0, stream>>>(o16, oexp, lse_part, splits, H, o_ext, lse_ext, out,
+                                                      lse_out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
