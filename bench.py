@@ -785,27 +785,28 @@ def summarize(args):
                                          "en": int(r["End_Timestamp"]), "c": {}})
             d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         disp = sorted(((d["name"], d["st"], d["en"], d["c"]) for d in by_disp.values()), key=lambda x: x[1])
-        agg = {}
+        per = {}
         for k, _, _, c in _labelled(disp):
-            a = agg.setdefault(k, {"n": 0})
-            a["n"] += 1
-            for cn, v in c.items():
-                a[cn] = a.get(cn, 0.0) + v
-        names = sorted({cn for a in agg.values() for cn in a if cn != "n"})
+            per.setdefault(k, []).append(c)
+        names = sorted({cn for v in per.values() for c in v for cn in c})
         lines = [f"# SQ counters: {cfg_desc}", "", "Commands (repository root on the GPU host as `$REPO`):",
                  "", "```", _commands_block(args), "```", "",
-                 "Sums per dispatch, averaged over the dispatches of each kernel.  MFMA busy = "
-                 "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8): GRBM_GUI_ACTIVE sums the "
-                 "8 XCDs' busy clocks, so /8 is the kernel's duration in clocks.", "",
+                 "Per-dispatch counter sums, median over the dispatches of each kernel (the bulk cache "
+                 "fill at setup is one dispatch of the append kernel and does not move its median).  "
+                 "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8), per "
+                 "dispatch, median: GRBM_GUI_ACTIVE sums the 8 XCDs' busy clocks, so /8 is the "
+                 "kernel's duration in clocks.  SQ_VALU_MFMA_BUSY_CYCLES counts the matrix pipe's busy "
+                 "clocks: 32 per 32 x 32 MFMA and 16 per 16 x 16 one in these kernels.", "",
                  "| kernel | n | MFMA busy | " + " | ".join(names) + " |",
                  "|---|---|---|" + "---|" * len(names)]
-        for k, a in sorted(agg.items(), key=lambda kv: -kv[1].get("GRBM_GUI_ACTIVE", 0) * kv[1]["n"]):
-            n = a["n"]
-            busy = "-"
-            if a.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in a:
-                busy = f"{a['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024.0 * a['GRBM_GUI_ACTIVE'] / 8.0):.3f}"
-            lines.append(f"| {k} | {n} | {busy} | " + " | ".join(f"{a.get(c, 0.0) / n:.4g}" for c in names)
-                         + " |")
+        def med(v):
+            return float(np.median(v)) if v else 0.0
+        for k, v in sorted(per.items(), key=lambda kv: -med([c.get("GRBM_GUI_ACTIVE", 0) for c in kv[1]])
+                           * len(kv[1])):
+            busy = [c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * c["GRBM_GUI_ACTIVE"] / 8.0) for c in v
+                    if c.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in c]
+            lines.append(f"| {k} | {len(v)} | {med(busy):.3f} | "
+                         + " | ".join(f"{med([c.get(cn, 0.0) for c in v]):.4g}" for cn in names) + " |")
         print("\n".join(lines))
         return 0
     print(f"unknown summary kind {kind}", file=sys.stderr)
