@@ -79,8 +79,7 @@ __device__ __forceinline__ void write_key8(const uint16_t* __restrict__ idx_key,
                                            uint8_t* __restrict__ key8_scale) {
   const uint32_t v = idx_key[((size_t)b * n_new + i) * DI + lane];
   uint32_t amax = v & 0x7FFFu;
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
+  amax = half_wave_max_u32(amax);
   const int sb = amax ? min(max(floor_log2_bf16(amax) - 8 + 127, 0), 254) : 0;
   const uint32_t code = ((v >> 15) << 7) | e4m3_code(v & 0x7FFFu, sb);
   key8[((size_t)b * cap + (size_t)j) * DI + lane] = (uint8_t)code;
@@ -111,8 +110,7 @@ __device__ __forceinline__ void append_entries(
   uint32_t amax = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) amax = max(amax, v[k] & 0x7FFFu);
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
+  amax = quad_max_u32(amax);
   const bool nonfinite = amax >= 0x7F80u;
   int sb = 0;
   if (!nonfinite && amax) sb = min(max(floor_log2_bf16(amax) - 2 + 127, 0), 254);
@@ -197,8 +195,7 @@ __device__ __forceinline__ void group_sum_unit(
 #pragma unroll
       for (int k = 0; k < 8; ++k) amax = max(amax, ((k & 1) ? (w4[k >> 1] >> 16) : w4[k >> 1]) & 0x7FFFu);
       amax = fresh[i] ? amax : 0u;
-      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
-      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
+      amax = quad_max_u32(amax);
       const int sb_new = amax ? min(max(floor_log2_bf16(amax) - 8 + 127, 0), 254) : 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {

@@ -97,12 +97,14 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void combine_kernel(const uint16_t*
     }
     const float le = (o_ext && l == 0) ? lse_ext[rh] : -__builtin_inff();
     float m = fmaxf(le, fmaxf(lv[0], lv[1]));
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
+    m = __uint_as_float(wave_allreduce(__float_as_uint(m), [](uint32_t a, uint32_t b) {
+      return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
     float sum = 0.f;
     if (m != -__builtin_inff()) sum = expf(lv[0] - m) + expf(lv[1] - m) + expf(le - m);
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) sum += __shfl_xor(sum, k, 64);
+    sum = __uint_as_float(wave_allreduce(__float_as_uint(sum), [](uint32_t a, uint32_t b) {
+      return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
     const float L = m == -__builtin_inff() ? -__builtin_inff() : m + logf(sum);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {

@@ -22,13 +22,75 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// Lane shuffles within a wave64 (compile to ds_bpermute / DPP as the compiler sees fit).
-__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+// Lane exchanges within a wave64 without LDS round trips: DPP swaps inside a
+// 16-lane row (quad xor 1 and xor 2, the 8-lane half-row mirror, the 16-lane
+// row mirror) and gfx950's row swaps (v_permlane16_swap: lane l meets l ^ 16;
+// v_permlane32_swap: l meets l ^ 32).  For a symmetric op, applying it to a
+// value and its partner at every step leaves the group's result in every lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;    // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;    // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7 - i within 8 lanes
+constexpr int DPP_ROW_MIRROR = 0x140;  // lane i <-> 15 - i within 16 lanes
 
-__device__ __forceinline__ float warp_max_xor(float v, int lo_mask_bits) {
-  // butterfly max over lanes whose ids differ in the low `lo_mask_bits` bits
-  for (int m = 1; m < (1 << lo_mask_bits); m <<= 1) v = fmaxf(v, shfl_xor(v, m));
-  return v;
+// op over the 8 lanes of an aligned group (3 DPP steps)
+template <typename F>
+__device__ __forceinline__ uint32_t group8_reduce(uint32_t x, F op) {
+  x = op(x, dpp_mov<DPP_QUAD_XOR1>(x));
+  x = op(x, dpp_mov<DPP_QUAD_XOR2>(x));
+  return op(x, dpp_mov<DPP_HALF_MIRROR>(x));
+}
+// op of lane l and lane l ^ 16, then of l and l ^ 32 (the row swaps)
+template <typename F>
+__device__ __forceinline__ uint32_t cross_rows_reduce(uint32_t x, F op) {
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op((uint32_t)a[0], (uint32_t)a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op((uint32_t)c[0], (uint32_t)c[1]);
+}
+// op over the whole wave, result in every lane
+template <typename F>
+__device__ __forceinline__ uint32_t wave_allreduce(uint32_t x, F op) {
+  x = group8_reduce(x, op);
+  x = op(x, dpp_mov<DPP_ROW_MIRROR>(x));
+  return cross_rows_reduce(x, op);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return wave_allreduce(x, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  return wave_allreduce(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return wave_allreduce(x, [](uint32_t a, uint32_t b) { return a + b; });
+}
+// max over an aligned group of 4 lanes (2 DPP steps), and over each 32-lane
+// half of the wave (lane l meets l ^ 16 last)
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t x) {
+  x = max(x, dpp_mov<DPP_QUAD_XOR1>(x));
+  return max(x, dpp_mov<DPP_QUAD_XOR2>(x));
+}
+__device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t x) {
+  auto op = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  x = group8_reduce(x, op);
+  x = op(x, dpp_mov<DPP_ROW_MIRROR>(x));
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return op((uint32_t)a[0], (uint32_t)a[1]);
+}
+// float max over an aligned group of 8 lanes
+__device__ __forceinline__ float group8_max(float v) {
+  return __uint_as_float(group8_reduce(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+// float sum of lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float cross_rows_sum(float v) {
+  return __uint_as_float(cross_rows_reduce(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 
 // Order-preserving map float -> uint32 (larger float -> larger key).  NaN and

@@ -134,13 +134,10 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
       float part = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) part += wv[i] * fmaxf(acc[i], 0.f);
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
+      part = cross_rows_sum(part);
       const int j = wbase + 16 * (t0 + u) + n;
       float s = j < jmax ? part : -__builtin_inff();
-      s = fmaxf(s, __shfl_xor(s, 1, 64));
-      s = fmaxf(s, __shfl_xor(s, 2, 64));
-      s = fmaxf(s, __shfl_xor(s, 4, 64));
+      s = group8_max(s);
       const int local_blk = (wave * PER_WAVE + 16 * (t0 + u) + n) / BLOCK;
       if ((lane == 0 || lane == 8) && x * (CH / BLOCK) + local_blk < n_out) out[local_blk] = s;
     }
@@ -344,8 +341,7 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(
   float part = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) part += wv[i] * fmaxf(acc[i], 0.f);
-  part += __shfl_xor(part, 16, 64);
-  part += __shfl_xor(part, 32, 64);
+  part = cross_rows_sum(part);
   if (kg == 0 && g < G) gscore[(size_t)row * G + g] = cnt > 0 ? part : -__builtin_inff();
 }
 

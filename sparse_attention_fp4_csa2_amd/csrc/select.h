@@ -3,6 +3,7 @@
 // described in topk.hip.
 #pragma once
 #include "device.h"
+#include <type_traits>
 
 namespace csa2 {
 namespace sel {
@@ -110,14 +111,11 @@ __device__ __forceinline__ void select_core(uint32_t (&key)[C], int n, int k, co
         if (key[c] >= 0x80000000u) kmin_nn = min(kmin_nn, key[c]), ++n_nn;
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-      nv += (uint32_t)__shfl_xor((int)nv, o, 64);
-      kmin_nn = min(kmin_nn, (uint32_t)__shfl_xor((int)kmin_nn, o, 64));
-      n_nn += (uint32_t)__shfl_xor((int)n_nn, o, 64);
-    }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    nv = wave_sum_u32(nv);
+    kmin_nn = wave_min_u32(kmin_nn);
+    n_nn = wave_sum_u32(n_nn);
     if (lane == 0) sred[wv][0] = kmin, sred[wv][1] = kmax, sred[wv][2] = nv, sred[wv][3] = kmin_nn,
                    sred[wv][4] = n_nn;
     __syncthreads();
@@ -238,11 +236,8 @@ __device__ __forceinline__ void select_core(uint32_t (&key)[C], int n, int k, co
         const uint32_t x = key[c];
         if (x && (x & m2) == prefix) bmin = min(bmin, x), bmax = max(bmax, x);
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        bmin = min(bmin, (uint32_t)__shfl_xor((int)bmin, o, 64));
-        bmax = max(bmax, (uint32_t)__shfl_xor((int)bmax, o, 64));
-      }
+      bmin = wave_min_u32(bmin);
+      bmax = wave_max_u32(bmax);
       if (lane == 0) sred[wv][0] = bmin, sred[wv][1] = bmax;
       __syncthreads();
       bmin = 0xffffffffu, bmax = 0u;
@@ -263,29 +258,32 @@ __device__ __forceinline__ void select_core(uint32_t (&key)[C], int n, int k, co
   const uint32_t tau = all ? 0u : ranked ? sh_tau : prefix;
   const uint32_t need_eq = all ? 0u : ranked ? sh_need : kleft;
 
-  uint32_t gt = 0, eq = 0;
+  // per-thread bit masks of the keys above tau and at tau (bit c = position i0 + c)
+  typedef typename std::conditional<(C > 32), unsigned long long, uint32_t>::type mask_t;
+  mask_t gtm = 0, eqm = 0;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
-    gt += key[c] > tau;
-    eq += key[c] == tau;
+    gtm |= (mask_t)(key[c] > tau) << c;
+    eqm |= (mask_t)(key[c] == tau) << c;
   }
+  const uint32_t gt = (uint32_t)__builtin_popcountll((unsigned long long)gtm);
+  const uint32_t eq = (uint32_t)__builtin_popcountll((unsigned long long)eqm);
   __shared__ uint32_t sbuf2[NW][2];
   uint32_t tot_gt, tot_eq, gt_pre, eq_pre;
   block_excl_scan2<TPB>(gt, eq, sbuf2, &gt_pre, &eq_pre, &tot_gt, &tot_eq);
-  uint32_t pos_out = gt_pre + min(eq_pre, need_eq);
+  // of this thread's keys at tau, the lowest-position ones that the earlier
+  // threads' ties leave room for are kept (counted up with compares only: a
+  // clamped need_eq - eq_pre was folded into an unclamped subtract that also
+  // stood in for min(eq_pre, need_eq) below)
+  mask_t sel = gtm;
   uint32_t eq_seen = eq_pre;
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    bool sel = key[c] > tau;
-    if (key[c] == tau) {
-      sel = eq_seen < need_eq;
-      ++eq_seen;
-    }
-    if (sel) {
-      const int i = i0 + c;
-      const int id = gsel ? gid * 64 + (i & 63) : i;
-      out[pos_out++] = id;
-    }
+  for (mask_t m = eqm; m != 0 && eq_seen < need_eq; m &= m - 1, ++eq_seen) sel |= m & (~m + 1);
+  // ascending positions: the set bits from the lowest up
+  uint32_t pos_out = gt_pre + min(eq_pre, need_eq);
+  for (mask_t m = sel; m != 0; m &= m - 1) {
+    const int c = __builtin_ctzll((unsigned long long)m);
+    const int i = i0 + c;
+    out[pos_out++] = gsel ? gid * 64 + (i & 63) : i;
   }
   const uint32_t total = tot_gt + min(tot_eq, need_eq);
   for (int i = (int)total + t; i < k; i += TPB) out[i] = -1;

@@ -122,8 +122,9 @@ __device__ __forceinline__ float pair_sum(float v) {
 }
 
 __device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = max(v, __shfl_xor(v, m, 64));
+  v = (int)wave_allreduce((uint32_t)v, [](uint32_t a, uint32_t b) {
+    return (uint32_t)max((int)a, (int)b);
+  });
   return v;
 }
 
