@@ -95,11 +95,13 @@ __device__ __forceinline__ float cross_rows_sum(float v) {
 
 // Order-preserving map float -> uint32 (larger float -> larger key).  NaN and
 // -inf both map to 0, which marks "not a candidate".
+// (selects only: the top-K kernels convert 16-64 scores per thread, and
+// early returns there became a branch per score)
 __device__ __forceinline__ uint32_t score_key(float s) {
-  uint32_t u = __float_as_uint(s);
-  if (s != s || s == -__builtin_inff()) return 0u;
-  if (s == 0.0f) return 0x80000000u;          // -0 and +0 are one score (a tie)
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(s);
+  uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  k = s == 0.0f ? 0x80000000u : k;             // -0 and +0 are one score (a tie)
+  return (s != s || s == -__builtin_inff()) ? 0u : k;
 }
 
 // Dequantise 8 MXFP4 codes (one dword; byte k holds element 2k in its low

@@ -104,12 +104,14 @@ __device__ __forceinline__ void select_core(uint32_t (&key)[C], int n, int k, co
     uint32_t kmin = 0xffffffffu, kmax = 0u, nv = 0, kmin_nn = 0xffffffffu, n_nn = 0;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      if (key[c]) {
-        kmin = min(kmin, key[c]);
-        kmax = max(kmax, key[c]);
-        ++nv;
-        if (key[c] >= 0x80000000u) kmin_nn = min(kmin_nn, key[c]), ++n_nn;
-      }
+      // selects, not branches (0 = not a candidate)
+      const uint32_t x = key[c];
+      const bool cand = x != 0u, nn = x >= 0x80000000u;
+      kmin = min(kmin, cand ? x : 0xffffffffu);
+      kmax = max(kmax, x);
+      nv += cand ? 1u : 0u;
+      kmin_nn = min(kmin_nn, nn ? x : 0xffffffffu);
+      n_nn += nn ? 1u : 0u;
     }
     kmin = wave_min_u32(kmin);
     kmax = wave_max_u32(kmax);
@@ -187,10 +189,15 @@ __device__ __forceinline__ void select_core(uint32_t (&key)[C], int n, int k, co
       // kleft-th largest of the bin publishes it (tau) and how many of its
       // equal keys are kept
       const uint32_t m2 = ~0u << pos;
+      // one slot reservation per thread for all of its keys in the bin
+      uint32_t nin = 0;
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const uint32_t x = key[c];
-        if (x && (x & m2) == prefix) rk_key[atomicAdd(&rk_n, 1u)] = x;
+      for (int c = 0; c < C; ++c) nin += (key[c] && (key[c] & m2) == prefix) ? 1u : 0u;
+      if (nin) {
+        uint32_t slot = atomicAdd(&rk_n, nin);
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          if (key[c] && (key[c] & m2) == prefix) rk_key[slot++] = key[c];
       }
       __syncthreads();
       const uint32_t cnt = rk_n;
