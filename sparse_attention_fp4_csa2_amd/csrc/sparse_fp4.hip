@@ -183,6 +183,18 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
     r.sc = __builtin_amdgcn_raw_buffer_load_b32(rec_rsrc, off + sc_off, 0, 0);
   };
 
+  // the query's bf16 values first (this lane's 64: dims 128dq + 64s + 32hh +
+  // [0, 32)), so their latency overlaps the block ids' and the first records'
+  const uint32_t qmask = head_ok ? 0xFFFFFFFFu : 0u;
+  uint4 qraw[2][4];
+  {
+    const uint16_t* qrow = p.q + ((size_t)row * p.H + (head_ok ? head : 0)) * D + 128 * dq + 32 * hh;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) qraw[s2][u] = reinterpret_cast<const uint4*>(qrow + 64 * s2)[u];
+  }
+
   // block ids of the first three tiles straight from memory, so that the first
   // records are in flight while the query is converted; the whole split's ids
   // are staged in LDS meanwhile
@@ -220,16 +232,13 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   uint32_t qsb = 0;       // scale bytes: [0] term 0 s0, [1] term 0 s1, [2] term 1 s0, [3] term 1 s1
   uint32_t qsb2 = 0;      // FP6: [0] term 2 s0, [1] term 2 s1
   bool wide = false;
-  const uint32_t qmask = head_ok ? 0xFFFFFFFFu : 0u;
   {
-    const uint16_t* qrow = p.q + ((size_t)row * p.H + (head_ok ? head : 0)) * D + 128 * dq + 32 * hh;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       float x[32];
-      const uint4* src = reinterpret_cast<const uint4*>(qrow + 64 * s);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint4 w = src[u];
+        const uint4 w = qraw[s][u];
         const uint32_t wv[4] = {w.x & qmask, w.y & qmask, w.z & qmask, w.w & qmask};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -280,10 +289,9 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   }
   const bool qb = __any(wide) != 0;     // wave-uniform: the bf16 form
   if (qb) {
-    const uint16_t* qrow = p.q + ((size_t)row * p.H + (head_ok ? head : 0)) * D + 128 * dq + 32 * hh;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const uint4 v = reinterpret_cast<const uint4*>(qrow + 64 * (m >> 2))[m & 3];
+      const uint4 v = qraw[m >> 2][m & 3];
       const int T = m >> 1, o = 4 * (m & 1);
       qt[T >> 1][T & 1][o] = (int)(v.x & qmask);
       qt[T >> 1][T & 1][o + 1] = (int)(v.y & qmask);
