@@ -449,7 +449,7 @@ def measure(name, args):
         "cold_breakdown_ms": {k: round(v, 4) for k, v in cold_bd.items()},
         "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
         "launches_per_step": per_step,
-        "kernels_per_layer": kernels_per_layer(cfg),
+        "kernels_per_layer": kernels_per_layer(cfg, wl._lib),
         "topk_unplanted_ms": round(topk_random, 4),
         "roofline": {"kernel": "csa2_attend_layer (attend_kernel: sparse + window branches; combine)",
                      "bound": "mfma", "achieved": round(tf(flops_layer, t_layer), 2),
@@ -589,16 +589,18 @@ def measured_peaks(torch, stream):
             "bf16_gemm_TFLOPs": round(2.0 * n ** 3 / (t_mm * 1e-3) / 1e12, 1)}
 
 
-def kernels_per_layer(cfg):
+def kernels_per_layer(cfg, lib=None):
     """Kernel launches of one layer's attention path, by layer mode (append not included).
 
     csa2_index_topk launches the indexer and the top-K (two-level: coarse scores,
-    group top-K, fine scores, top-K); csa2_attend_layer always launches two
-    (both branches in one kernel, then the combine).  Reuse layers run only
-    the latter."""
+    group top-K, fine scores, top-K); csa2_attend_layer launches both branches
+    in one kernel, then a combine unless that kernel leaves a single partial
+    per (row, head) (the library reports which).  Reuse layers run only the
+    latter."""
     index = 4 if cfg.top_groups else 2
+    attend = lib.attend_layer_launches(cfg.B, cfg.Q, cfg.H, cfg.K, cfg.W) if lib is not None else 2
     modes = sorted(set(cfg.layers)) if cfg.name != "prefill" else ["F"]
-    return {m: (index + 2 if m in ("F", "R") else 2) for m in modes}
+    return {m: (index + attend if m in ("F", "R") else attend) for m in modes}
 
 
 def workload_config(cfg, rows, index_keys="bf16"):

@@ -222,9 +222,13 @@ size_t csa2_swa_merge_ws(int B, int Q, int H, int W);
 /* One attention layer in a single call: the sparse branch of csa2_sparse_attn
  * and the window branch of csa2_swa_merge, merged by log-sum-exp (which is one
  * softmax over the selected entries and the window tokens together).  Both
- * branches write their split-K partials into ws and one combine pass produces
- * out / lse_out; no intermediate sparse-only output exists.  Arguments as in
- * the two calls above (q_pos also fixes the window, swa_pos0 NULL = 0).
+ * branches run in one launch and write split-K partials into ws (where a
+ * workgroup runs a window split after its sparse split, it continues the same
+ * softmax and leaves one partial for both), then one combine pass produces
+ * out / lse_out; with a single partial per (row, head) the launch writes
+ * out / lse_out itself and no combine runs.  No intermediate sparse-only
+ * output exists.  Arguments as in the two calls above (q_pos also fixes the
+ * window, swa_pos0 NULL = 0).
  *   out fp32 [B][Q][H][512]; lse_out fp32 [B][Q][H]
  *   ws: >= csa2_attend_layer_ws(B, Q, H, top_k, W) bytes */
 int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* idx,
@@ -233,6 +237,9 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
                       int B, int Q, int H, int cap, int top_k, int W, int Lw, float scale,
                       float* out, float* lse_out, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_attend_layer_ws(int B, int Q, int H, int top_k, int W);
+/* Kernel launches csa2_attend_layer makes for these sizes (1 or 2; 0 for
+ * invalid sizes): a report for callers that count launches per layer. */
+int csa2_attend_layer_launches(int B, int Q, int H, int top_k, int W);
 
 /* csa2_attend_layer in two phases, so that the window branch -- which needs no
  * selection -- can run on a second stream while the indexer and top-K run.

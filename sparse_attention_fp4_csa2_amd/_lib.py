@@ -37,6 +37,7 @@ _SIGS = {
     "csa2_attend_layer": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                _P, _P, _P, _SZ, _P]),
     "csa2_attend_layer_ws": (_SZ, [_I, _I, _I, _I, _I]),
+    "csa2_attend_layer_launches": (_I, [_I, _I, _I, _I, _I]),
     "csa2_attend_layer_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "csa2_attend_layer_sparse": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P,
                                       _SZ, _P]),
@@ -232,6 +233,10 @@ def swa_merge(q, swa_kv, swa_len, W, scale, o_sparse, lse_sparse, out, lse_out, 
 
 def attend_layer_ws(B, Q, H, top_k, W):
     return load().csa2_attend_layer_ws(B, Q, H, top_k, W)
+
+
+def attend_layer_launches(B, Q, H, top_k, W):
+    return load().csa2_attend_layer_launches(B, Q, H, top_k, W)
 
 
 def attend_layer(q, cache, idx, count, n_entries, swa_kv, swa_len, W, scale, out, lse_out, ws,

@@ -316,6 +316,13 @@ static int layer_window_splits(int rows, int H, int s_sparse, int W) {
   return layer_window_inline(rows, H, s_sparse, W) ? (s_sparse < wt ? s_sparse : wt) : window_splits(rows, H, wt);
 }
 
+int csa2_attend_layer_launches(int B, int Q, int H, int top_k, int W) {
+  if (B <= 0 || Q <= 0 || H <= 0 || top_k <= 0 || W <= 0) return 0;
+  const int rows = B * Q;
+  const int s_sparse = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
+  return layer_window_inline(rows, H, s_sparse, W) && s_sparse == 1 ? 1 : 2;
+}
+
 size_t csa2_attend_layer_ws(int B, int Q, int H, int top_k, int W) {
   if (B <= 0 || Q <= 0 || H <= 0 || top_k <= 0 || W <= 0) return 0;
   const int rows = B * Q;
@@ -400,23 +407,30 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
   const int rows = B * Q;
   const int s_sparse = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
   const int s_window = layer_window_splits(rows, H, s_sparse, W);
-  const int total = s_sparse + s_window;
-  if (total > 128) return CSA2_ERR_UNSUPPORTED;
+  const bool inl = layer_window_inline(rows, H, s_sparse, W);
+  // inline: sparse split s also runs window split s on the same softmax state,
+  // so the layer leaves s_sparse partials (with one split, the output itself);
+  // otherwise sparse -> splits [0, s_sparse), window -> [s_sparse, total)
+  const int total = inl ? s_sparse : s_sparse + s_window;
+  if (s_sparse + s_window > 128) return CSA2_ERR_UNSUPPORTED;
   const PartWs l = part_ws_layout(rows, total, H);
   hipStream_t st = as_stream(stream);
-  // sparse branch -> splits [0, s_sparse); window -> [s_sparse, total); one combine
   AttnParams p{};
   p.q = q; p.cache = cache; p.idx = idx; p.count = count; p.n_entries = n_entries;
   p.top_k = top_k; p.cap = cap; p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.splits = s_sparse;
-  set_partials(p, ws, l, total, 0);
+  if (total == 1) {
+    p.o_out = out; p.lse_out = lse_out; p.out_splits = 1; p.split_base = 0;
+  } else {
+    set_partials(p, ws, l, total, 0);
+  }
   AttnParams pw = p;
   pw.cache = nullptr; pw.idx = nullptr; pw.count = nullptr; pw.n_entries = nullptr;
   pw.swa = swa_kv; pw.swa_len = swa_len; pw.swa_pos0 = swa_pos0; pw.W = W; pw.Lw = Lw;
   pw.splits = s_window; pw.split_base = s_sparse;
-  int rc = launch_attend(p, pw, layer_window_inline(rows, H, s_sparse, W), st);   // both branches in one launch
-  if (!rc) rc = combine_partials(ws, l, rows, total, H, nullptr, nullptr, out, lse_out, st);
+  int rc = launch_attend(p, pw, inl, st);   // both branches in one launch
+  if (!rc && total > 1) rc = combine_partials(ws, l, rows, total, H, nullptr, nullptr, out, lse_out, st);
   return launch_status(rc);
 }
 

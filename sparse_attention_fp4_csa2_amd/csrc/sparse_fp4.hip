@@ -138,8 +138,13 @@ constexpr int BUF_DWORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
 
 }  // namespace
 
-// One workgroup's share: rows `row`, split `split` of p.splits, head group hgi
-__device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int split, int hgi, Lds& lds) {
+// One workgroup's share: rows `row`, split `split` of p.splits, head group hgi.
+// after_loop(oacc, m_run, l_lane, base_o) runs when the tile loop is done,
+// before the epilogue, and may continue the softmax state (the fused launch
+// runs its window share there, so both branches leave one partial).
+template <typename AfterLoop>
+__device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int split, int hgi, Lds& lds,
+                                            AfterLoop after_loop) {
   const int tid = threadIdx.x;
   const int dq = tid >> 6;        // wave: latent dims [128dq, 128dq + 128)
   const int lane = tid & 63;
@@ -500,6 +505,7 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
     const int k = (t_end - 1 - t_begin) & 3;
     finish_prev((t_end - 1) & 1, k == 0 ? r0 : k == 1 ? ra : k == 2 ? rb : rx);
   }
+  after_loop(oacc, m_run, l_lane, base_o);
 
   // ---- finalize: denominators across the 4 quarter owners -----------------
   const float lq = pair_sum(l_lane);
@@ -551,15 +557,17 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   int unit, hgi;
   map_unit(blockIdx.x, n_units, hgroups, p.splits > 1, unit, hgi);
   if (unit >= n_units) return;
-  sparse_unit(p, unit / p.splits, unit % p.splits, hgi, lds);
+  sparse_unit(p, unit / p.splits, unit % p.splits, hgi, lds, [](floatx16(&)[4], float&, float&, int&) {});
 }
 
 // Both branches of one layer in one launch, in one of two arrangements:
 //  * inline (pw.splits <= ps.splits): every sparse workgroup (row, split s,
 //    head group) then runs the window's split s of the same row and head
-//    group, when s < pw.splits.  The window work is spread over all the
-//    sparse workgroups, so it adds a few tiles to each of them instead of
-//    running as short workgroups after them.
+//    group, when s < pw.splits, continuing its online softmax: the two
+//    branches leave one partial per sparse split (pw's outputs are unused),
+//    and a layer with one sparse split needs no combine.  The window work is
+//    spread over all the sparse workgroups, so it adds a few tiles to each of
+//    them instead of running as short workgroups after them.
 //  * after: the grid is the sparse workgroups followed by the window's, so
 //    the window runs in the slots the sparse workgroups free as they finish.
 __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_units, int hgroups,
@@ -574,10 +582,23 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_uni
     map_unit(blockIdx.x, n_units, hgroups, ps.splits > 1, unit, hgi);
     if (unit >= n_units) return;
     const int row = unit / ps.splits, split = unit - row * ps.splits;
-    sparse_unit(ps, row, split, hgi, lds.s);
     if (inline_window && split < pw.splits) {
-      __syncthreads();                      // the window reuses the LDS
-      win::window_unit(pw, row, split, hgi, lds.w);
+      // this workgroup's window split continues the softmax of its sparse
+      // split: one partial for both.  The accumulator leaves its V base for
+      // plain units first (an exact power of two), as the bf16 window rows
+      // are not rescaled.
+      sparse_unit(ps, row, split, hgi, lds.s,
+                  [&](floatx16 (&oacc)[4], float& m_run, float& l_lane, int& base_o) {
+                    const float rs = ldexpf(1.f, base_o - VBIAS);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) oacc[mt] *= rs;
+                    base_o = VBIAS;
+                    __syncthreads();          // the window reuses the LDS
+                    win::window_tiles(pw, row, split, hgi, lds.w, oacc, m_run, l_lane);
+                    __syncthreads();          // the epilogue's LDS overlaps the window's
+                  });
+    } else {
+      sparse_unit(ps, row, split, hgi, lds.s, [](floatx16(&)[4], float&, float&, int&) {});
     }
   } else {
     const int wn = pw.rows * pw.splits;

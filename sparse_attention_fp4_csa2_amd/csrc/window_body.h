@@ -74,8 +74,13 @@ struct WinRaw {
   uint4 k[8];      // dims 128dq + 64hh + 8s + [0, 8) of token e, s < 8
 };
 
-// One workgroup's share: row `row`, split `split` of p.splits, head group hgi
-__device__ __forceinline__ void window_unit(const AttnParams& p, int row, int split, int hgi, WinLds& lds) {
+// The window tiles of one workgroup's share (row `row`, split `split` of
+// p.splits, head group hgi), continuing the online softmax state it is given:
+// O^T in oacc (plain units), the running max and this lane's denominator.  The
+// fused launch passes the state its sparse share left, so the two branches
+// leave one partial; window_unit starts from an empty state.
+__device__ __forceinline__ void window_tiles(const AttnParams& p, int row, int split, int hgi, WinLds& lds,
+                                             floatx16 (&oacc)[4], float& m_run, float& l_lane) {
   const int tid = threadIdx.x;
   const int dq = tid >> 6;        // wave: latent dims [128dq, 128dq + 128)
   const int lane = tid & 63;
@@ -134,11 +139,6 @@ __device__ __forceinline__ void window_unit(const AttnParams& p, int row, int sp
       lds.sp[dq][j][lane] = floatx4{sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3]};
   };
 
-  floatx16 oacc[4];       // O^T: [dims 128dq + 32mt + 8(i/4) + 4hh + i%4][head]
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) oacc[mt] = floatx16{};
-  float m_run = M_INIT;   // running max of z * log2(e), per head (lane pair)
-  float l_lane = 0.f;     // softmax denominator over this lane's quarter tokens
   uint2 vt[2][4][2];      // V^T A fragments of the previous tile, [ks2][mt][half]
   uint4 phf[2], plf[2];   // P^T B fragments (hi, lo) of the previous tile, [ks2]
   bool have_pv = false;
@@ -267,6 +267,23 @@ __device__ __forceinline__ void window_unit(const AttnParams& p, int row, int sp
     }
   }
   if (have_pv) issue_pv();
+}
+
+// One workgroup's share: row `row`, split `split` of p.splits, head group hgi
+__device__ __forceinline__ void window_unit(const AttnParams& p, int row, int split, int hgi, WinLds& lds) {
+  const int tid = threadIdx.x;
+  const int dq = tid >> 6;
+  const int lane = tid & 63;
+  const int e = lane & 31;
+  const int hh = lane >> 5;
+  const int head = 32 * hgi + e;
+  const bool head_ok = head < p.H;
+  floatx16 oacc[4];       // O^T: [dims 128dq + 32mt + 8(i/4) + 4hh + i%4][head]
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) oacc[mt] = floatx16{};
+  float m_run = M_INIT;   // running max of z * log2(e), per head (lane pair)
+  float l_lane = 0.f;     // softmax denominator over this lane's quarter tokens
+  window_tiles(p, row, split, hgi, lds, oacc, m_run, l_lane);
 
   // ---- finalize: denominators across the 4 quarter owners -----------------
   const float lq = pair_sum(l_lane);

@@ -333,13 +333,17 @@ def test_attend_layer_causal_rows():
 
 def test_two_phase_layer_on_two_streams_matches_one_call():
     # csa2_attend_layer_window on a second stream + csa2_attend_layer_sparse on
-    # the first (joined by an event) gives csa2_attend_layer's bytes exactly;
-    # twice in a row on one workspace, the second call with other queries
+    # the first (joined by an event) against csa2_attend_layer and the oracle;
+    # twice in a row on one workspace, the second call with other queries.  The
+    # one launch folds the window into the sparse workgroups' softmax (one
+    # partial per split) where the phases keep a partial per branch, so the two
+    # agree to rounding, not bit for bit; both meet the bar against the oracle
     lib = _lib()
     rng = rng_for(52)
     B, Q, H, N, K, W, Lw = 2, 3, 64, 4096, 128, 96, 96
     latent = normal_bf16(rng, (B, N, 512))
     cache = gpu_cache(latent, N)
+    cache_np = [mxfp4.build_records(latent[b], N) for b in range(B)]
     swa = normal_bf16(rng, (B, Lw, 512))
     pos0 = [2 * N - 60, 2 * N - 90]
     q_pos = np.array([[2 * N - 50, 2 * N - 10, 2 * N + 20], [2 * N - 90, 2 * N - 1, 2 * N + 5]], np.int32)
@@ -365,8 +369,16 @@ def test_two_phase_layer_on_two_streams_matches_one_call():
         main.wait_event(done)
         lib.attend_layer_sparse(d_q, cache, d_idx, d_cnt, d_n, W, SCALE, out, lse, ws, q_pos=d_qpos, stream=main)
         torch.cuda.synchronize()
-        assert np.array_equal(host(out), ref_o), f"call {call}: out differs from csa2_attend_layer"
-        assert np.array_equal(host(lse), ref_l), f"call {call}: lse differs from csa2_attend_layer"
+        got_o, got_l = host(out), host(lse)
+        assert_close_rms(got_o, ref_o, what=f"call {call}: two phases vs one call")
+        assert_lse_close(got_l, ref_l, tol=1e-4)
+        for b in range(B):
+            for r in range(Q):
+                ro, rl = modes.attend_row(q[b, r], cache_np[b], idx[b, r], int(count[b, r]), int(n_entries[b]),
+                                          swa[b], Lw, W, q_pos=int(q_pos[b, r]), swa_pos0=pos0[b])
+                assert_close_rms(got_o[b, r], ro, what=f"call {call} row {b},{r}: two phases")
+                assert_close_rms(ref_o[b, r], ro, what=f"call {call} row {b},{r}: one call")
+                assert_lse_close(got_l[b, r], rl)
 
 
 @pytest.mark.parametrize("B,H", [(2, 64), (8, 40)])
@@ -395,8 +407,10 @@ def test_one_launch_layer_reuses_its_workspace(B, H):
 
 
 def test_run_layer_side_stream_matches_one_stream():
-    # modes.run_layer with the window branch forked onto a second stream gives
-    # the same bytes as the one-stream call, for a Full and a Reuse layer
+    # modes.run_layer with the window branch forked onto a second stream (the
+    # two-phase calls) against the one-stream call (one launch), for a Full and
+    # a Reuse layer: the same selection bit for bit, the outputs to rounding (the
+    # one launch may fold the window into the sparse partials)
     from sparse_attention_fp4_csa2_amd import modes as gm
     cfg = CONFIGS["tiny"]
     x = decode_inputs(cfg)
@@ -413,8 +427,12 @@ def test_run_layer_side_stream_matches_one_stream():
         gm.run_layer("U", bu, cache, q, swa, swa_len, prev=prev, side_stream=s)
         torch.cuda.synchronize()
         res.append([host(t) for t in (bf.idx, bf.count, bf.out, bf.lse_out, bu.out, bu.lse_out)])
-    for a, b in zip(*res):
-        assert np.array_equal(a, b)
+    (i1, c1, o1, l1, u1, m1), (i2, c2, o2, l2, u2, m2) = res
+    assert np.array_equal(i1, i2) and np.array_equal(c1, c2)
+    for a, b, what in ((o1, o2, "Full out"), (u1, u2, "Reuse out")):
+        assert_close_rms(b, a, what=f"side stream vs one stream: {what}")
+    for a, b in ((l1, l2), (m1, m2)):
+        assert_lse_close(b, a, tol=1e-4)
 
 
 def _scale_bf16(bits, k):
