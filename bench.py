@@ -451,7 +451,8 @@ def measure(name, args):
         "launches_per_step": per_step,
         "kernels_per_layer": kernels_per_layer(cfg, wl._lib),
         "topk_unplanted_ms": round(topk_random, 4),
-        "roofline": {"kernel": "csa2_attend_layer (attend_kernel: sparse + window branches; combine)",
+        "roofline": {"kernel": "csa2_attend_layer (attend_kernel: sparse + window branches; then the combine "
+                               "unless one partial per (row, head) remains)",
                      "bound": "mfma", "achieved": round(tf(flops_layer, t_layer), 2),
                      "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf(flops_layer, t_layer) / PEAK_FP16_TFLOPS, 4),
@@ -720,15 +721,14 @@ def summarize(args):
             lines.append(f"| {k} | {len(w)} | {fmt(float(np.median(w)) if w else None)} | "
                          f"{fmt(float(np.mean(w)) if w else None)} | {len(c)} | "
                          f"{fmt(float(np.mean(c)) if c else None)} | {min(w + c):.2f} |")
-        att = by.get("attend_kernel"), by.get("combine_kernel (csa2_attend_layer)")
-        if all(att) and bench is not None:
-            wm = float(np.median(att[0]["warm"])) + float(np.median(att[1]["warm"]))
-            cm = (float(np.mean(att[0]["cold"])) + float(np.mean(att[1]["cold"]))) if att[0]["cold"] and \
-                att[1]["cold"] else None
+        att = [v for v in (by.get("attend_kernel"), by.get("combine_kernel (csa2_attend_layer)")) if v]
+        if by.get("attend_kernel") and bench is not None:
+            wm = sum(float(np.median(a["warm"])) for a in att)
+            cm = sum(float(np.mean(a["cold"])) for a in att) if all(a["cold"] for a in att) else None
             ev_w = bench.get("breakdown_ms", {}).get("attend_layer")
             ev_c = bench.get("cold_breakdown_ms", {}).get("attend_layer")
-            lines += ["", "The roofline's unit, one `csa2_attend_layer` call = `attend_kernel` + its "
-                      "`combine_kernel`:", "",
+            lines += ["", "The roofline's unit, one `csa2_attend_layer` call = `attend_kernel`"
+                      + (" + its `combine_kernel`" if len(att) > 1 else " (one launch: no combine)") + ":", "",
                       f"- warm: trace medians {wm:.2f} µs; the traced run's own HIP-event time per call "
                       f"{ev_w * 1000:.2f} µs" if ev_w is not None else f"- warm: trace medians {wm:.2f} µs"]
             if cm is not None:
@@ -762,11 +762,12 @@ def summarize(args):
             per[counter] = {k: float(np.median(v)) for k, v in vals.items()}
         f_fac = copy_bytes / 1024.0 / per["FETCH_SIZE"]["copy"]
         w_fac = copy_bytes / 1024.0 / per["WRITE_SIZE"]["copy"]
-        call = ("attend_kernel", "combine_kernel (csa2_attend_layer)")
+        # the call's launches (the combine is absent when the launch leaves one partial)
+        call = [k for k in ("attend_kernel", "combine_kernel (csa2_attend_layer)") if k in per["FETCH_SIZE"]]
         fetch = sum(per["FETCH_SIZE"][k] for k in call) * 1024 * f_fac
         write = sum(per["WRITE_SIZE"][k] for k in call) * 1024 * w_fac
         cfg = CONFIGS[args.config]
-        rec = {"kernel": "csa2_attend_layer call = attend_kernel + combine_kernel",
+        rec = {"kernel": "csa2_attend_layer call = " + " + ".join(k.split(" (")[0] for k in call),
                "workload": cfg_desc, "kernel_sources_sha256": kernel_digest(),
                "bytes_per_call": int(round(fetch + write)), "fetch_bytes_per_call": int(round(fetch)),
                "write_bytes_per_call": int(round(write)),
