@@ -104,8 +104,9 @@ int csa2_append_fp4(const uint16_t* latent, const uint16_t* idx_key, const int32
  * Keeps the top_k candidates by (score desc, block id asc) and writes them
  * ascending, padded with -1, plus their count.
  * Two-level (top_groups > 0, needs group_sum, q_pos == NULL): group g = blocks
- * [64g, 64g+64) scores its mean key (group_sum / present count); the best
- * top_groups groups are kept, and blocks are scored only inside them.
+ * [64g, 64g+64) scores its mean key (group_sum / present count, formed in fp32
+ * and taken into the scoring MFMA as bf16 hi + lo: about 16 significant bits);
+ * the best top_groups groups are kept, and blocks are scored only inside them.
  *   q_idx bf16 [B][Q][Hi][64]; w fp32 [B][Q][Hi]; key_cache bf16 [B][cap][64]
  *   n_entries int32 [B]; q_pos int32 [B][Q] or NULL
  *   idx int32 [B][Q][top_k]; count int32 [B][Q]
