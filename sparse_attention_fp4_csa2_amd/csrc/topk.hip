@@ -63,19 +63,20 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ sco
   sel::select_core<TPB, C, RANGE>(key, n, k, gsel, n_gsel, row, idx + (size_t)row * k, count + row);
 }
 
-// n <= 65536.  Rows of up to 1024 scores run on 256 threads with fixed digits
-// (one short pass), or, when there are too few rows to fill the chip, one
-// score per thread on 1024 threads with range-relative digits (8 rows of 1024
-// coarse group scores, whose few exponents crowd fixed digits into a handful
-// of bins); longer ones use range-relative digits, on 256 threads, or on
-// 512-1024 when rows are few (there one row's latency is the cost: 32 rows of
-// 4096 scores 8.4 -> 7.4 us on 512 threads).
+// n <= 65536.  Rows of up to 1024 scores run on 256 threads, 4 scores each:
+// with fixed digits (one short pass) when rows are many, with range-relative
+// digits when they are too few to fill the chip (8 rows of 1024 coarse group
+// scores, whose few exponents crowd fixed digits into a handful of bins; one
+// score per thread on 1024 threads took 5.4 us there, 4 on 256 take 4.6 us).
+// Longer rows use range-relative digits, on 256 threads, or on 512-1024 when
+// rows are few (there one row's latency is the cost: 32 rows of 4096 scores
+// 8.4 -> 7.4 us on 512 threads).
 int launch_topk(const float* scores, int rows, int n, int k, const int32_t* gsel, int n_gsel,
                 int32_t* idx, int32_t* count, hipStream_t stream) {
   const int vec = (n % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
 #define CSA2_TOPK(T, C, R) \
   topk_kernel<T, C, R><<<rows, T, 0, stream>>>(scores, n, k, vec, gsel, n_gsel, idx, count)
-  if (n <= 1024 && rows < 128) CSA2_TOPK(1024, 1, true);
+  if (n <= 1024 && rows < 128) CSA2_TOPK(256, 4, true);
   else if (n <= 256 * 4) CSA2_TOPK(256, 4, false);
   else if (n <= 512 * 8 && rows < 128) CSA2_TOPK(512, 8, true);
   else if (n <= 256 * 16) CSA2_TOPK(256, 16, true);
