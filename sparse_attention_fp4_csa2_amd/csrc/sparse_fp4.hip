@@ -554,6 +554,11 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
 
 __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_units, int hgroups) {
   __shared__ Lds lds;
+  // every argument the prologue needs, in one round of scalar loads: left to
+  // itself the compiler loads them in three dependent rounds, each waited on
+  // where it is first used (the early return splits the prologue)
+  asm volatile("" ::"s"(p.q), "s"(p.cache), "s"(p.idx), "s"(p.count), "s"(p.n_entries), "s"(p.q_pos),
+               "s"(p.top_k), "s"(p.cap), "s"(p.Q), "s"(p.H), "s"(p.splits), "s"(p.scale_log2));
   int unit, hgi;
   map_unit(blockIdx.x, n_units, hgroups, p.splits > 1, unit, hgi);
   if (unit >= n_units) return;
@@ -577,6 +582,10 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_uni
     Lds s;
     win::WinLds w;
   } lds;
+  // every argument the sparse prologue needs, in one round of scalar loads (as
+  // in sparse_fp4_kernel; decode attention calls 1-2 us faster)
+  asm volatile("" ::"s"(ps.q), "s"(ps.cache), "s"(ps.idx), "s"(ps.count), "s"(ps.n_entries), "s"(ps.q_pos),
+               "s"(ps.top_k), "s"(ps.cap), "s"(ps.Q), "s"(ps.H), "s"(ps.splits), "s"(ps.scale_log2));
   int unit, hgi;
   if ((int)blockIdx.x < n_sparse_wg) {
     map_unit(blockIdx.x, n_units, hgroups, ps.splits > 1, unit, hgi);
