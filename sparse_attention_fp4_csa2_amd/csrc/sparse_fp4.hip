@@ -449,10 +449,11 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   // Pipeline, one barrier per tile.  Tile t, between barriers B(t-1) and B(t)
   // (rc = tile t+1's records, loaded during tile t-1; rl receives tile t+2's,
   // requested first so that a whole tile of work hides their latency):
-  //   reads: S(t) partials, P(t-1), flags(t-1), V^T(t-1) (all written before B(t-1))
-  //   P(t-1).V(t-1) (after a rare max move) | softmax(t): P(t), flags(t) written
-  //   V(t+1) written, Q.K(t+1), S(t+1) partial written
-  // S, P, flags and the V tile are double-buffered by tile parity.
+  //   reads: S(t) partials, P(t-1), flags(t-1) (all written before B(t-1))
+  //   P(t-1).V(t-1), V dequantised from tile t-1's codes, still in registers
+  //   (after a rare max move) | softmax(t): P(t), flags(t) written |
+  //   Q.K(t+1), S(t+1) partial written
+  // S, P and flags are double-buffered by tile parity; V never enters LDS.
   auto tile_step = [&](int t, const Raw& rp, Raw& rc, Raw& rl) {
     const int buf = t & 1;
     if (t & 1) __builtin_amdgcn_s_setprio(1);    // wave priority alternates by tile

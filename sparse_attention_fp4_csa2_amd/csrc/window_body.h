@@ -1,8 +1,9 @@
 // Window-attention workgroup body (bf16 rows of each sequence's sliding
 // window), shared by the window kernel and the fused attention launch.
 //
-// The same organisation as the MXFP4 sparse kernel, on bf16 rows.  One workgroup = (row, split, group of 32 heads), 4 waves; wave dq owns
-// latent dims [128dq, 128dq + 128) for all 32 heads; two workgroups share a CU.
+// The same organisation as the MXFP4 sparse kernel, on bf16 rows.  One
+// workgroup = (row, split, group of 32 heads), 4 waves; wave dq owns latent
+// dims [128dq, 128dq + 128) for all 32 heads; two workgroups share a CU.
 // A tile is 32 window tokens.  Per tile:
 //  * Q.K: lane (token e = lane%32, half hh) holds 64 contiguous dims of e's row
 //    as the A operand of v_mfma_f32_32x32x16_bf16 (8 k-steps), the query the
