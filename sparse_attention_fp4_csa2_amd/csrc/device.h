@@ -168,7 +168,8 @@ __device__ __forceinline__ void store_o16_slice(const floatx16 (&acc)[4], float 
 // groups of a split, dispatched together, share their reads).  With one split
 // (many rows per sequence, as in prefill) unit u goes to XCD u % 8 and its
 // head groups to ids 8 apart: measured to fetch a quarter of the L2 misses of
-// the contiguous order there.
+// the contiguous order there.  The split combine places its workgroups on the
+// XCD of their row under the contiguous order (launch_combine).
 __device__ __forceinline__ void map_unit(int L, int n_units, int hgroups, bool several_splits, int& unit,
                                          int& hgi) {
   if (several_splits) {
