@@ -456,8 +456,6 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   // S, P and flags are double-buffered by tile parity; V never enters LDS.
   auto tile_step = [&](int t, const Raw& rp, Raw& rc, Raw& rl) {
     const int buf = t & 1;
-    if (t & 1) __builtin_amdgcn_s_setprio(1);    // wave priority alternates by tile
-    else __builtin_amdgcn_s_setprio(0);
     const bool more = t + 1 < t_end;
     fetch(id_next, rl);
     id_next = read_id(t + 3);
