@@ -310,6 +310,38 @@ def test_attend_layer_decode_matches_joint_softmax(H):
     assert_lse_close(lse, rl)
 
 
+@pytest.mark.parametrize("B,N,K,W", [(4, 2048, 64, 128),     # few rows: window inside the sparse workgroups
+                                     (32, 1024, 64, 512)])   # 32 rows: window workgroups after the sparse ones
+def test_attend_layer_empty_branches(B, N, K, W):
+    # rows cycle through: both branches, empty window, empty selection, both
+    # empty (nothing visible: out 0, lse -inf); the merge must take a lone
+    # branch unchanged and the empty row must stay exactly zero
+    rng = rng_for(50 + B)
+    H, Lw = 64, W
+    latent = normal_bf16(rng, (B, N, 512))
+    cache = gpu_cache(latent, N)
+    cache_np = [mxfp4.build_records(latent[b], N) for b in range(B)]
+    q = normal_bf16(rng, (B, 1, H, 512))
+    swa = normal_bf16(rng, (B, Lw, 512))
+    swa_len = np.array([[Lw, 0, W // 2 + 3, 0][b % 4] for b in range(B)], np.int32)
+    count = np.array([[[K], [K - 5], [0], [0]][b % 4] for b in range(B)], np.int32)
+    n_entries = np.full(B, N, np.int32)
+    idx = np.full((B, 1, K), -1, np.int32)
+    for b in range(B):
+        c = int(count[b, 0])
+        idx[b, 0, :c] = np.sort(rng.choice(N // 8, c, replace=False))
+    out, lse = gpu_layer(q, cache, idx, count, n_entries, swa, swa_len, W)
+    ro = np.zeros((B, 1, H, 512))
+    rl = np.zeros((B, 1, H))
+    for b in range(B):
+        ro[b, 0], rl[b, 0] = modes.attend_row(q[b, 0], cache_np[b], idx[b, 0], int(count[b, 0]), N,
+                                              swa[b], int(swa_len[b]), W)
+    assert_close_rms(out, ro)
+    assert_lse_close(lse, rl)
+    for b in range(3, B, 4):
+        assert (out[b] == 0).all() and np.isneginf(lse[b]).all(), f"row {b}: nothing visible"
+
+
 def test_attend_layer_causal_rows():
     rng = rng_for(41)
     B, Q, H, N, K, W = 1, 6, 64, 4096, 96, 32
