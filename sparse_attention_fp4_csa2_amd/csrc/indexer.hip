@@ -236,11 +236,11 @@ __global__ __launch_bounds__(256) void index_rows_kernel(
     const int j = e + col;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      floatx16 acc = floatx16{};
-      if (e < lim_max) {
+      // keys past every row's limit load as zeros and their scores are masked
+      // below, so the chain runs unconditionally (no zeroed accumulator)
+      floatx16 acc = mfma32_bf16(qa[a][0], kv[0], floatx16{});
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma32_bf16(qa[a][ks], kv[ks], acc);
-      }
+      for (int ks = 1; ks < 4; ++ks) acc = mfma32_bf16(qa[a][ks], kv[ks], acc);
       // this lane's heads 4hh..4hh+3 of the set's rows r4 = 0..3
       float ps[4];
 #pragma unroll
