@@ -84,16 +84,16 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void combine_kernel(const uint16_t*
   const int t = threadIdx.x;
   const int g = t >> 6, l = t & 63;
   const size_t rh = (size_t)row * H + h;
-  const size_t part0 = (size_t)row * splits * H + h;              // split s at part0 + s * H
+  const size_t part0 = rh * splits;                               // split s at part0 + s
   const float* lp = lse_part + part0;
 
   // this wave's partials: splits g + 4i, lane dims [8l, 8l + 8); the first
   // CMB_PF requested before the weights exist (they do not depend on them)
   typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
   const uint4* src = reinterpret_cast<const uint4*>(o16 + part0 * D) + l;
-  const size_t stride = (size_t)CMB_WAVES * H * D / 8;           // 4 splits, in uint4
+  const size_t stride = (size_t)CMB_WAVES * D / 8;               // 4 splits, in uint4
   const int n_mine = g < splits ? (splits - g + CMB_WAVES - 1) / CMB_WAVES : 0;
-  src += (size_t)g * H * D / 8;
+  src += (size_t)g * D / 8;
   uint4 buf[CMB_PF];
 #pragma unroll
   for (int i = 0; i < CMB_PF; ++i) buf[i] = i < n_mine ? src[(size_t)i * stride] : make_uint4(0u, 0u, 0u, 0u);
@@ -105,8 +105,8 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void combine_kernel(const uint16_t*
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int s = l + 64 * j;
-      lv[j] = s < splits ? lp[(size_t)s * H] : -__builtin_inff();
-      ev[j] = s < splits ? oexp[part0 + (size_t)s * H] : 0;
+      lv[j] = s < splits ? lp[s] : -__builtin_inff();
+      ev[j] = s < splits ? oexp[part0 + s] : 0;
     }
     const float le = (o_ext && l == 0) ? lse_ext[rh] : -__builtin_inff();
     float m = fmaxf(le, fmaxf(lv[0], lv[1]));

@@ -66,12 +66,12 @@ struct AttnParams {
   int Q, H, rows, splits;
   float scale_log2;         // scale * log2(e)
   // output: either the final fp32 o (o_out, one split) or split-K partials:
-  // o16_out fp16 [rows][out_splits][H][512] with o = o16 * 2^oexp_out per
+  // o16_out fp16 [rows][H][out_splits][512] with o = o16 * 2^oexp_out per
   // (row, split, head), so the partials take half the bytes of fp32
   float* o_out;             // [rows][H][512] final o, or null
-  uint16_t* o16_out;        // [rows][out_splits][H][512] partial o, or null
-  int32_t* oexp_out;        // [rows][out_splits][H] power-of-two exponent of o16_out
-  float* lse_out;           // [rows][out_splits][H]
+  uint16_t* o16_out;        // [rows][H][out_splits][512] partial o, or null
+  int32_t* oexp_out;        // [rows][H][out_splits] power-of-two exponent of o16_out
+  float* lse_out;           // [rows][H][out_splits] (one split: the final [rows][H])
   int out_splits;           // split stride of the outputs (>= split_base + splits)
   int split_base;           // this launch writes splits [split_base, split_base + splits)
 };

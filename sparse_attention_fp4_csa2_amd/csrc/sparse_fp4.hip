@@ -514,9 +514,9 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   const float il = l > 0.f ? 1.f / l : 0.f;
   if (head_ok && dq == 0 && hh == 0) {
     const float lse = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
-    p.lse_out[((size_t)row * p.out_splits + p.split_base + split) * p.H + head] = lse;
+    p.lse_out[((size_t)row * p.H + head) * p.out_splits + p.split_base + split] = lse;
   }
-  const size_t orow = ((size_t)row * p.out_splits + p.split_base + split) * p.H + head;
+  const size_t orow = ((size_t)row * p.H + head) * p.out_splits + p.split_base + split;
   if (!p.o16_out) {                  // one split: the final fp32 o
     if (head_ok) {
       const float f = ldexpf(il, base_o - VBIAS);

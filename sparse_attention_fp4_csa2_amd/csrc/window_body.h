@@ -292,7 +292,7 @@ __device__ __forceinline__ void window_unit(const AttnParams& p, int row, int sp
   __syncthreads();
   const float l = (lds.lsum[0][e] + lds.lsum[1][e]) + (lds.lsum[2][e] + lds.lsum[3][e]);
   const float il = l > 0.f ? 1.f / l : 0.f;
-  const size_t orow = ((size_t)row * p.out_splits + p.split_base + split) * p.H + head;
+  const size_t orow = ((size_t)row * p.H + head) * p.out_splits + p.split_base + split;
   if (head_ok && dq == 0 && hh == 0) {
     const float lse = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
     p.lse_out[orow] = lse;
