@@ -64,7 +64,8 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode1m",
-                    choices=["tiny", "decode64k", "decode1m", "layers128k", "prefill", "specdec64k"])
+                    choices=["tiny", "decode64k", "decode1m", "layers128k", "prefill", "specdec64k",
+                             "specdec64k_h16", "prefill_h16"])
     ap.add_argument("--also", default=None,
                     help="comma-separated workloads timed after the headline one and carried in the same "
                          "JSON line (default for decode1m: decode64k,layers128k; '' for none)")
@@ -309,7 +310,7 @@ def make_workload(name, device="cuda", key_format="bf16"):
     from synth import CONFIGS, decode_inputs, layers_inputs, prefill_inputs, specdec_inputs
     from synth.gen import LayerInputs
     cfg = CONFIGS[name]
-    if name == "prefill":
+    if cfg.prior:
         p = prefill_inputs(cfg)
         return cfg, p, PrefillWorkload(cfg, p, device, key_format)
     if len(cfg.layers) > 1:
@@ -437,7 +438,7 @@ def measure(name, args):
     topk_random = warm_ms(lambda: wl._lib.topk(rnd, cfg.K, t_idx, t_cnt, stream=stream), reps)
     del rnd, scratch, flush_out
 
-    prefill = cfg.name == "prefill"
+    prefill = cfg.prior > 0
     res = {
         "value": round(rows / (ms_cold * 1e-3), 1),
         "unit": "tokens/s" if prefill else "queries/s",
@@ -600,14 +601,15 @@ def kernels_per_layer(cfg, lib=None):
     latter."""
     index = 4 if cfg.top_groups else 2
     attend = lib.attend_layer_launches(cfg.B, cfg.Q, cfg.H, cfg.K, cfg.W) if lib is not None else 2
-    modes = sorted(set(cfg.layers)) if cfg.name != "prefill" else ["F"]
+    modes = sorted(set(cfg.layers)) if not cfg.prior else ["F"]
     return {m: (index + attend if m in ("F", "R") else attend) for m in modes}
 
 
 def workload_config(cfg, rows, index_keys="bf16"):
-    if cfg.name == "prefill":
+    if cfg.prior:
         desc = (f"prefill: {cfg.Q} query tokens after {cfg.prior} cached entries (+{cfg.Q // 2} "
-                f"appended), H {cfg.H}, indexer {cfg.Hi}x64, top-K {cfg.K} per row, window {cfg.W}, causal")
+                f"appended), H {cfg.H}, indexer {cfg.Hi}x64, top-K {cfg.K} per row, window {cfg.W}, causal"
+                + (f", query rows in runs of {cfg.q_run} per indexer direction" if cfg.q_run > 1 else ""))
     else:
         desc = (f"{cfg.name}: decode, B {cfg.B}, H {cfg.H}, {cfg.N} MXFP4 entries/seq "
                 f"({cfg.N // 8} blocks of 8), indexer {cfg.Hi}x64"
@@ -849,7 +851,7 @@ def cpu_baseline(cfg, host_in, budget_s):
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     nb = cfg.cap // 8
     done, elapsed = 0, 0.0
-    if cfg.name == "prefill":
+    if cfg.prior:
         p = host_in
         Q = p["q"].shape[1]
         N = int(p["n_entries"][0])

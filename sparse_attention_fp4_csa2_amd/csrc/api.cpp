@@ -224,7 +224,7 @@ int csa2_topk(const float* scores, int rows, int n, int k, int32_t* idx, int32_t
 size_t csa2_sparse_attn_ws(int B, int Q, int H, int top_k) {
   if (B <= 0 || Q <= 0 || H <= 0 || top_k <= 0) return 0;
   const int rows = B * Q;
-  const int s = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
+  const int s = sparse_attn_splits(B, Q, H, top_k);
   if (s <= 1) return 0;
   return part_ws_layout(rows, s, H).total;
 }
@@ -240,7 +240,7 @@ int csa2_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx
   if (H > CSA2_MAX_HEADS) return CSA2_ERR_UNSUPPORTED;
   if ((size_t)cap / CSA2_BLOCK * CSA2_RECORD_BYTES > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
   const int rows = B * Q;
-  const int splits = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
+  const int splits = sparse_attn_splits(B, Q, H, top_k);
   const size_t need = csa2_sparse_attn_ws(B, Q, H, top_k);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WS_TOO_SMALL;
   if (need > 0 && !aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
@@ -306,28 +306,29 @@ int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa
 // ones (128 rows of 4 per sequence: 334.6 -> 326.5 us).  Otherwise it keeps
 // its own split count and workgroups after the sparse ones: inline it cost
 // up to ~1 us more there, plus a combine over more splits.
-static bool layer_window_inline(int rows, int H, int s_sparse, int W) {
+static bool layer_window_inline(int rows, int Q, int H, int s_sparse, int W) {
+  if (sparse_rows_per_tile(H, Q) > 1) return false;   // row tiles: the window's own workgroups
   const int wt = (W + 31) / 32;
   const int s_own = window_splits(rows, H, wt);
   return s_sparse >= wt || (wt + s_own - 1) / s_own > 8;
 }
-static int layer_window_splits(int rows, int H, int s_sparse, int W) {
+static int layer_window_splits(int rows, int Q, int H, int s_sparse, int W) {
   const int wt = (W + 31) / 32;
-  return layer_window_inline(rows, H, s_sparse, W) ? (s_sparse < wt ? s_sparse : wt) : window_splits(rows, H, wt);
+  return layer_window_inline(rows, Q, H, s_sparse, W) ? (s_sparse < wt ? s_sparse : wt) : window_splits(rows, H, wt);
 }
 
 int csa2_attend_layer_launches(int B, int Q, int H, int top_k, int W) {
   if (B <= 0 || Q <= 0 || H <= 0 || top_k <= 0 || W <= 0) return 0;
   const int rows = B * Q;
-  const int s_sparse = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
-  return layer_window_inline(rows, H, s_sparse, W) && s_sparse == 1 ? 1 : 2;
+  const int s_sparse = sparse_attn_splits(B, Q, H, top_k);
+  return layer_window_inline(rows, Q, H, s_sparse, W) && s_sparse == 1 ? 1 : 2;
 }
 
 size_t csa2_attend_layer_ws(int B, int Q, int H, int top_k, int W) {
   if (B <= 0 || Q <= 0 || H <= 0 || top_k <= 0 || W <= 0) return 0;
   const int rows = B * Q;
-  const int s_sparse = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
-  return part_ws_layout(rows, s_sparse + layer_window_splits(rows, H, s_sparse, W), H).total;
+  const int s_sparse = sparse_attn_splits(B, Q, H, top_k);
+  return part_ws_layout(rows, s_sparse + layer_window_splits(rows, Q, H, s_sparse, W), H).total;
 }
 
 int csa2_attend_layer_window(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa_len,
@@ -343,8 +344,8 @@ int csa2_attend_layer_window(const uint16_t* q, const uint16_t* swa_kv, const in
   if (!ws || ws_bytes < need) return CSA2_ERR_WS_TOO_SMALL;
   if (!aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
   const int rows = B * Q;
-  const int s_sparse = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
-  const int s_window = layer_window_splits(rows, H, s_sparse, W);
+  const int s_sparse = sparse_attn_splits(B, Q, H, top_k);
+  const int s_window = layer_window_splits(rows, Q, H, s_sparse, W);
   const int total = s_sparse + s_window;
   if (total > 128) return CSA2_ERR_UNSUPPORTED;
   AttnParams pw{};
@@ -370,8 +371,8 @@ int csa2_attend_layer_sparse(const uint16_t* q, const uint8_t* cache, const int3
   if (!ws || ws_bytes < need) return CSA2_ERR_WS_TOO_SMALL;
   if (!aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
   const int rows = B * Q;
-  const int s_sparse = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
-  const int s_window = layer_window_splits(rows, H, s_sparse, W);
+  const int s_sparse = sparse_attn_splits(B, Q, H, top_k);
+  const int s_window = layer_window_splits(rows, Q, H, s_sparse, W);
   const int total = s_sparse + s_window;
   if (total > 128) return CSA2_ERR_UNSUPPORTED;
   const PartWs l = part_ws_layout(rows, total, H);
@@ -405,9 +406,9 @@ int csa2_attend_layer(const uint16_t* q, const uint8_t* cache, const int32_t* id
   if (!ws || ws_bytes < need) return CSA2_ERR_WS_TOO_SMALL;
   if (!aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
   const int rows = B * Q;
-  const int s_sparse = sparse_fp4_splits(rows, H, attn_n_tiles(top_k));
-  const int s_window = layer_window_splits(rows, H, s_sparse, W);
-  const bool inl = layer_window_inline(rows, H, s_sparse, W);
+  const int s_sparse = sparse_attn_splits(B, Q, H, top_k);
+  const int s_window = layer_window_splits(rows, Q, H, s_sparse, W);
+  const bool inl = layer_window_inline(rows, Q, H, s_sparse, W);
   // inline: sparse split s also runs window split s on the same softmax state,
   // so the layer leaves s_sparse partials (with one split, the output itself);
   // otherwise sparse -> splits [0, s_sparse), window -> [s_sparse, total)

@@ -42,6 +42,7 @@
 //    other tile, which evens out the two.
 #include "device.h"
 #include "launch.h"
+#include "select.h"
 #include "window_body.h"
 
 namespace csa2 {
@@ -59,13 +60,19 @@ typedef int int32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 
 struct Lds {
-  floatx4 sp[2][4][4][64];         // [buffer][wave][quarter][lane] partial S^T  32 KB
+  union {
+    floatx4 sp[2][4][4][64];       // [buffer][wave][quarter][lane] partial S^T  32 KB
+    uint32_t bm[8192];             // row tiles' prologue: each row's selected-block bitmap
+  };
   uint16_t pb[2][32 * PROW];       // [buffer][head * PROW + slot] fp16 P        5 KB
   float qmax[2][4][32];            // [buffer][wave][head] quarter max of z*log2e
   int flag[2][4];                  // [buffer][wave] quarter needs a max move
   float lsum[4][32];               // epilogue: per-wave softmax denominators
   int emax[4][32];                 // epilogue: per-wave exponent of the largest |o|
   int32_t blk[MAX_SPLIT_BLOCKS];   // this split's selected block ids           8 KB
+  uint8_t memb[MAX_SPLIT_BLOCKS];  // row tiles: bit r = row r of the tile selected the item
+  uint32_t scan[4];                // row tiles: per-wave sums of the union count
+  int dup;                         // row tiles: some row lists a block twice
 };
 
 // A = 32 E2M1 codes, B = 32 E2M1 codes (byte 0 of each scale operand)
@@ -131,44 +138,76 @@ __device__ __forceinline__ int wave_max_int(int v) {
 struct Raw {
   uint4 c0, c1;    // 32 bytes of codes: this wave's dims 64s + 32hh + [0, 32), s = 0, 1
   uint32_t sc;     // scale bytes of groups 4dq .. 4dq + 3
-  int valid;
+  int valid;       // the entry is present and visible; row tiles: bit r = to row r of the tile
 };
 
 constexpr int BUF_DWORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
 
 }  // namespace
 
-// One workgroup's share: rows `row`, split `split` of p.splits, head group hgi.
+// One workgroup's share: split `split` of p.splits, head group hgi, of one
+// tile of rows.  R == 1: the tile is row `row`, its 32 columns the heads 32 hgi
+// + [0, 32).  R > 1 (few heads per row): the tile is group `row` of R
+// consecutive rows of one sequence (the sequence's rows in groups of R, the
+// last group possibly shorter), column e = row e / (32 / R) of the group and
+// head (32 / R) hgi + e % (32 / R); the tile attends the union of its rows'
+// selections, each block gathered and its V dequantised once for every row
+// that selected it, and each column masked to its own row's blocks and causal
+// limit.  Should a row list a block twice (or the cache be too large for the
+// union's bitmap) the rows' lists are run one after the other instead, each
+// block once per row that lists it, as a single row would count it.
 // after_loop(oacc, m_run, l_lane, base_o) runs when the tile loop is done,
 // before the epilogue, and may continue the softmax state (the fused launch
 // runs its window share there, so both branches leave one partial).
-template <typename AfterLoop>
+template <int R, typename AfterLoop>
 __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int split, int hgi, Lds& lds,
                                             AfterLoop after_loop) {
+  constexpr int HP = 32 / R;      // heads per row among the tile's 32 columns
   const int tid = threadIdx.x;
   const int dq = tid >> 6;        // wave: latent dims [128dq, 128dq + 128)
   const int lane = tid & 63;
-  const int e = lane & 31;        // Q.K: entry of the tile;  S^T, P^T, O^T: head of the group
+  const int e = lane & 31;        // Q.K: entry of the tile;  S^T, P^T, O^T: column of the tile
   const int hh = lane >> 5;
-  const int b = row / p.Q;
-  const int head = 32 * hgi + e;
-  const bool head_ok = head < p.H;
+  int b, q0, nr;                  // the tile's sequence, first query and row count
+  if (R == 1) {
+    b = row / p.Q;
+    q0 = row - b * p.Q;
+    nr = 1;
+  } else {
+    const int ngq = (p.Q + R - 1) / R;
+    b = row / ngq;
+    q0 = (row - b * ngq) * R;
+    nr = min(R, p.Q - q0);
+  }
+  const int row0 = b * p.Q + q0;
+  const int rsub = e / HP;        // this lane's column: row row0 + rsub, head HP hgi + e % HP
+  const int row_l = row0 + rsub;
+  const int head = HP * hgi + e % HP;
+  const bool head_ok = head < p.H && rsub < nr;
 
-  int n_items = p.count[row];
-  n_items = n_items < 0 ? 0 : (n_items > p.top_k ? p.top_k : n_items);
-  const int t_pos = p.q_pos ? p.q_pos[row] : 0;
-  const int n_tiles = (n_items + 3) / 4;
-  // splits partition the row's top_k slots, not its count, so the first block
-  // ids are requested before the count arrives; the count only ends the loop
-  const int tps = ((p.top_k + 3) / 4 + p.splits - 1) / p.splits;
-  const int t_begin = split * tps;
-  const int t_end = min(n_tiles, t_begin + tps);
   const int n_ent = p.n_entries[b];
   const int nb_cap = p.cap / BLOCK;
-  // entries below lim are present and visible (entry j covers raw positions
-  // 2j and 2j + 1; a causal query at raw position t sees 2j + 1 <= t)
-  const int lim = p.q_pos ? min(n_ent, (t_pos + 1) >> 1) : n_ent;
-  const int n_items_split = min(n_items, 4 * t_end);
+  int n_items, t_begin, t_end, n_items_split, lim = n_ent;
+  int lim_r[R];                   // row tiles: entries below lim_r[r] are present and visible to row r
+  if (R == 1) {
+    n_items = p.count[row];
+    n_items = n_items < 0 ? 0 : (n_items > p.top_k ? p.top_k : n_items);
+    const int t_pos = p.q_pos ? p.q_pos[row] : 0;
+    const int n_tiles = (n_items + 3) / 4;
+    // splits partition the row's top_k slots, not its count, so the first block
+    // ids are requested before the count arrives; the count only ends the loop
+    const int tps = ((p.top_k + 3) / 4 + p.splits - 1) / p.splits;
+    t_begin = split * tps;
+    t_end = min(n_tiles, t_begin + tps);
+    // entries below lim are present and visible (entry j covers raw positions
+    // 2j and 2j + 1; a causal query at raw position t sees 2j + 1 <= t)
+    lim = p.q_pos ? min(n_ent, (t_pos + 1) >> 1) : n_ent;
+    n_items_split = min(n_items, 4 * t_end);
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      lim_r[r] = r < nr ? (p.q_pos ? min(n_ent, (p.q_pos[row0 + r] + 1) >> 1) : n_ent) : 0;
+  }
   // this sequence's records as a raw buffer: ids outside [0, nb_cap) (the -1
   // padding included) fall outside it and load zeros
   const __amdgpu_buffer_rsrc_t rec_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -180,12 +219,35 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
     const int item = 4 * t + (e >> 3);
     return item < n_items_split ? lds.blk[min(item - 4 * t_begin, MAX_SPLIT_BLOCKS - 1)] : -1;
   };
-  auto fetch = [&](int blk, Raw& r) {
-    r.valid = (uint32_t)blk < (uint32_t)nb_cap && blk * BLOCK + (e & 7) < lim;
+  auto read_mb = [&](int t) -> int {
+    const int item = 4 * t + (e >> 3);
+    return R > 1 && item < n_items_split ? lds.memb[min(item - 4 * t_begin, MAX_SPLIT_BLOCKS - 1)] : 0;
+  };
+  auto fetch = [&](int blk, int mb, Raw& r) {
+    const int ent = blk * BLOCK + (e & 7);
+    r.valid = (uint32_t)blk < (uint32_t)nb_cap && ent < lim;
+    if (R > 1) {
+      int ok = 0;
+#pragma unroll
+      for (int k = 0; k < R; ++k) ok |= (r.valid && ((mb >> k) & 1) && ent < lim_r[k]) ? 1 << k : 0;
+      r.valid = ok;
+    }
     const uint32_t off = (uint32_t)blk * RECORD;
     r.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rec_rsrc, off + code_off, 0, 0));
     r.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rec_rsrc, off + code_off + 32, 0, 0));
     r.sc = __builtin_amdgcn_raw_buffer_load_b32(rec_rsrc, off + sc_off, 0, 0);
+  };
+  // the tile's entry mask for this lane's column: row tiles combine each
+  // entry's presence with its row bits and the column row's causal limit
+  auto tile_mask = [&](const Raw& r) -> uint32_t {
+    if (R == 1) return (uint32_t)__ballot(r.valid);
+    uint32_t vm = 0;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const uint32_t m = (uint32_t)__ballot((r.valid >> k) & 1);
+      vm = rsub == k ? m : vm;
+    }
+    return vm;
   };
 
   // the query's bf16 values first (this lane's 64: dims 128dq + 64s + 32hh +
@@ -193,29 +255,126 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   const uint32_t qmask = head_ok ? 0xFFFFFFFFu : 0u;
   uint4 qraw[2][4];
   {
-    const uint16_t* qrow = p.q + ((size_t)row * p.H + (head_ok ? head : 0)) * D + 128 * dq + 32 * hh;
+    const uint16_t* qrow = p.q + ((size_t)(head_ok ? row_l : row0) * p.H + (head_ok ? head : 0)) * D +
+                           128 * dq + 32 * hh;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int u = 0; u < 4; ++u) qraw[s2][u] = reinterpret_cast<const uint4*>(qrow + 64 * s2)[u];
   }
 
-  // block ids of the first three tiles straight from memory, so that the first
-  // records are in flight while the query is converted; the whole split's ids
-  // are staged in LDS meanwhile
-  const int32_t* const idx_row = p.idx + (size_t)row * p.top_k;
-  auto mem_id = [&](int t) -> int {
-    const int item = 4 * t + (e >> 3);
-    const int v = idx_row[min(item, p.top_k - 1)];   // unconditional: the loads overlap
-    return item < n_items_split ? v : -1;
-  };
-  const int i_beg = 4 * t_begin;
-  const int stage0 = idx_row[min(i_beg + tid, p.top_k - 1)];
   Raw r0, ra, rb, rx;     // raw tiles (see the tile loop)
-  fetch(mem_id(t_begin), r0);
-  fetch(mem_id(t_begin + 1), ra);
-  int id_next = mem_id(t_begin + 2);   // this lane's block id for the next fetch (read a tile early)
-
+  int id_next, mb_next = 0;   // this lane's block id (and row bits) for the next fetch (read a tile early)
+  const int32_t* const idx_row = p.idx + (size_t)row0 * p.top_k;
+  const int i_beg = 4 * (R == 1 ? t_begin : 0);
+  int stage0 = 0;
+  if (R == 1) {
+    // block ids of the first three tiles straight from memory, so that the
+    // first records are in flight while the query is converted; the whole
+    // split's ids are staged in LDS meanwhile
+    auto mem_id = [&](int t) -> int {
+      const int item = 4 * t + (e >> 3);
+      const int v = idx_row[min(item, p.top_k - 1)];   // unconditional: the loads overlap
+      return item < n_items_split ? v : -1;
+    };
+    stage0 = idx_row[min(i_beg + tid, p.top_k - 1)];
+    fetch(mem_id(t_begin), 0, r0);
+    fetch(mem_id(t_begin + 1), 0, ra);
+    id_next = mem_id(t_begin + 2);
+  } else {
+    // ---- row tile: the union of the rows' selections ----------------------
+    // a bitmap of each row's blocks in LDS (over the S buffers, unused until
+    // the first Q.K), then the union enumerated in ascending block order; the
+    // split's share of it goes to blk, with each item's row bits in memb
+    constexpr int BMW = 8192 / R;              // bitmap words per row
+    const bool use_bm = nb_cap <= 32 * BMW;
+    const int nw = (nb_cap + 31) >> 5;
+    int nsel[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = r < nr ? p.count[row0 + r] : 0;
+      nsel[r] = c < 0 ? 0 : (c > p.top_k ? p.top_k : c);
+    }
+    if (use_bm)
+      for (int i = tid; i < R * nw; i += 256) lds.bm[(i / nw) * BMW + i % nw] = 0;
+    if (tid == 0) lds.dup = 0;
+    __syncthreads();
+    if (use_bm) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        for (int i = tid; i < nsel[r]; i += 256) {
+          const int id = idx_row[(size_t)r * p.top_k + i];
+          if ((uint32_t)id < (uint32_t)nb_cap) {
+            const uint32_t bit = 1u << (id & 31);
+            if (atomicOr(&lds.bm[r * BMW + (id >> 5)], bit) & bit) lds.dup = 1;
+          }
+        }
+    }
+    __syncthreads();
+    auto set_split = [&](int u) {
+      n_items = u;
+      const int nt = (u + 3) / 4;
+      const int tps = (nt + p.splits - 1) / p.splits;
+      t_begin = split * tps;
+      t_end = min(nt, t_begin + tps);
+      n_items_split = min(u, 4 * t_end);
+    };
+    if (use_bm && lds.dup == 0) {
+      // thread t counts the union's blocks in words [wpt t, wpt t + wpt)
+      const int wpt = (nw + 255) / 256;
+      uint32_t cnt = 0;
+      for (int k = 0; k < wpt; ++k) {
+        const int w = wpt * tid + k;
+        if (w < nw) {
+          uint32_t u = 0;
+#pragma unroll
+          for (int r = 0; r < R; ++r) u |= lds.bm[r * BMW + w];
+          cnt += __builtin_popcount(u);
+        }
+      }
+      uint32_t total;
+      uint32_t rank = sel::block_excl_scan<256>(cnt, lds.scan, &total);
+      set_split((int)total);
+      const uint32_t lo = 4 * t_begin, hi = n_items_split;
+      for (int k = 0; k < wpt && rank < hi; ++k) {
+        const int w = wpt * tid + k;
+        if (w >= nw) break;
+        uint32_t wr[R], u = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) wr[r] = lds.bm[r * BMW + w], u |= wr[r];
+        for (; u != 0 && rank < hi; u &= u - 1, ++rank) {
+          if (rank < lo) continue;
+          const int bit = __builtin_ctz(u);
+          int mb = 0;
+#pragma unroll
+          for (int r = 0; r < R; ++r) mb |= (int)((wr[r] >> bit) & 1u) << r;
+          lds.blk[rank - lo] = 32 * w + bit;
+          lds.memb[rank - lo] = (uint8_t)mb;
+        }
+      }
+    } else {
+      // the rows' own lists one after the other (item k of the concatenation:
+      // row r's entry k - (the earlier rows' counts))
+      int u = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) u += nsel[r];
+      set_split(u);
+      for (int k = 4 * t_begin + tid; k < n_items_split; k += 256) {
+        int r = 0, kk = k;
+#pragma unroll
+        for (int j = 0; j < R - 1; ++j)
+          if (r == j && kk >= nsel[j]) kk -= nsel[j], r = j + 1;
+        const int id = idx_row[(size_t)r * p.top_k + kk];
+        lds.blk[k - 4 * t_begin] = (uint32_t)id < (uint32_t)nb_cap ? id : -1;
+        lds.memb[k - 4 * t_begin] = (uint8_t)(1 << r);
+      }
+    }
+    __syncthreads();      // the union's share staged; the bitmaps (over S) are free again
+    fetch(read_id(t_begin), read_mb(t_begin), r0);
+    fetch(read_id(t_begin + 1), read_mb(t_begin + 1), ra);
+    id_next = read_id(t_begin + 2);
+    mb_next = read_mb(t_begin + 2);
+  }
   // ---- query -----------------------------------------------------------
   // FP6 form: three E2M3 terms per 32-dim block.  Lane (head, hh), k-step s:
   // FP6 value k = dim 128dq + 64s + 32hh + k.  Each lane's 32 values are one
@@ -305,9 +464,11 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
     }
   }
 
-  if (i_beg + tid < n_items_split) lds.blk[tid] = stage0;
-  for (int i = i_beg + tid + 256; i < n_items_split; i += 256) lds.blk[i - i_beg] = idx_row[i];
-  __syncthreads();
+  if (R == 1) {
+    if (i_beg + tid < n_items_split) lds.blk[tid] = stage0;
+    for (int i = i_beg + tid + 256; i < n_items_split; i += 256) lds.blk[i - i_beg] = idx_row[i];
+    __syncthreads();
+  }
 
   // ---- tile helpers -----------------------------------------------------
   // largest scale byte of the wave's groups in the tile (every fetched entry,
@@ -379,7 +540,7 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
     base_v = raise_base(r0, 13);     // >= 13: the dequantising MFMA's B scale byte 267 - base fits
     base_o = base_v;
     qk_s(t_begin & 1, r0);
-    vmask_cur = (uint32_t)__ballot(r0.valid);
+    vmask_cur = tile_mask(r0);
   }
   __syncthreads();
 
@@ -457,8 +618,9 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   auto tile_step = [&](int t, const Raw& rp, Raw& rc, Raw& rl) {
     const int buf = t & 1;
     const bool more = t + 1 < t_end;
-    fetch(id_next, rl);
+    fetch(id_next, mb_next, rl);
     id_next = read_id(t + 3);
+    mb_next = read_mb(t + 3);
     floatx4 sw[4];
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) sw[w2] = lds.sp[buf][w2][dq][lane];
@@ -486,7 +648,7 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
     base_prev = base_v;           // the base tile t's V is dequantised with
     if (more) {
       qk_s(buf ^ 1, rc);
-      vmask_cur = (uint32_t)__ballot(rc.valid);
+      vmask_cur = tile_mask(rc);
       base_v = base_next;
     }
     __syncthreads();
@@ -514,9 +676,9 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   const float il = l > 0.f ? 1.f / l : 0.f;
   if (head_ok && dq == 0 && hh == 0) {
     const float lse = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
-    p.lse_out[((size_t)row * p.H + head) * p.out_splits + p.split_base + split] = lse;
+    p.lse_out[((size_t)row_l * p.H + head) * p.out_splits + p.split_base + split] = lse;
   }
-  const size_t orow = ((size_t)row * p.H + head) * p.out_splits + p.split_base + split;
+  const size_t orow = ((size_t)row_l * p.H + head) * p.out_splits + p.split_base + split;
   if (!p.o16_out) {                  // one split: the final fp32 o
     if (head_ok) {
       const float f = ldexpf(il, base_o - VBIAS);
@@ -551,6 +713,8 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   }
 }
 
+// R rows per tile (1, 2, 4); a unit is (tile, split)
+template <int R>
 __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_units, int hgroups) {
   __shared__ Lds lds;
   // every argument the prologue needs, in one round of scalar loads: left to
@@ -561,7 +725,7 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
   int unit, hgi;
   map_unit(blockIdx.x, n_units, hgroups, p.splits > 1, unit, hgi);
   if (unit >= n_units) return;
-  sparse_unit(p, unit / p.splits, unit % p.splits, hgi, lds, [](floatx16(&)[4], float&, float&, int&) {});
+  sparse_unit<R>(p, unit / p.splits, unit % p.splits, hgi, lds, [](floatx16(&)[4], float&, float&, int&) {});
 }
 
 // Both branches of one layer in one launch, in one of two arrangements:
@@ -574,6 +738,8 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
 //    them instead of running as short workgroups after them.
 //  * after: the grid is the sparse workgroups followed by the window's, so
 //    the window runs in the slots the sparse workgroups free as they finish.
+// Row tiles (R > 1) take the second arrangement only.
+template <int R>
 __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_units, int hgroups,
                                                         int n_sparse_wg, AttnParams pw, int whgroups,
                                                         int inline_window) {
@@ -590,12 +756,12 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_uni
     map_unit(blockIdx.x, n_units, hgroups, ps.splits > 1, unit, hgi);
     if (unit >= n_units) return;
     const int row = unit / ps.splits, split = unit - row * ps.splits;
-    if (inline_window && split < pw.splits) {
+    if (R == 1 && inline_window && split < pw.splits) {
       // this workgroup's window split continues the softmax of its sparse
       // split: one partial for both.  The accumulator leaves its V base for
       // plain units first (an exact power of two), as the bf16 window rows
       // are not rescaled.
-      sparse_unit(ps, row, split, hgi, lds.s,
+      sparse_unit<R>(ps, row, split, hgi, lds.s,
                   [&](floatx16 (&oacc)[4], float& m_run, float& l_lane, int& base_o) {
                     const float rs = ldexpf(1.f, base_o - VBIAS);
 #pragma unroll
@@ -606,7 +772,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_uni
                     __syncthreads();          // the epilogue's LDS overlaps the window's
                   });
     } else {
-      sparse_unit(ps, row, split, hgi, lds.s, [](floatx16(&)[4], float&, float&, int&) {});
+      sparse_unit<R>(ps, row, split, hgi, lds.s, [](floatx16(&)[4], float&, float&, int&) {});
     }
   } else {
     const int wn = pw.rows * pw.splits;
@@ -629,26 +795,73 @@ int sparse_fp4_splits(int rows, int H, int n_tiles) {
   return s;
 }
 
+// Rows per tile: a row fills the tile's 32 MFMA columns with its own heads when
+// H > 16; with 16 or fewer heads (one GPU's share of 64 heads split 4 or 8
+// ways) 2 or 4 consecutive rows of a sequence share the columns and every
+// gathered block.
+int sparse_rows_per_tile(int H, int Q) {
+  int r = H <= 8 ? 4 : (H <= 16 ? 2 : 1);
+  while (r > 1 && r > Q) r >>= 1;
+  return r;
+}
+
+// Split count of a sparse launch over B sequences of Q rows: the rule above
+// over its tiles (a row tile attends up to R selections, so its splits keep
+// each split's share of the union within the LDS staging)
+int sparse_attn_splits(int B, int Q, int H, int top_k) {
+  const int r = sparse_rows_per_tile(H, Q);
+  const int tiles = B * ((Q + r - 1) / r);
+  const int hp = 32 / r;
+  return sparse_fp4_splits(tiles * ((H + hp - 1) / hp), 32, (r * top_k + 3) / 4);
+}
+
+namespace {
+// grid of a sparse launch: (tile, split) units x head groups, the units a multiple of 8
+struct SparseGrid {
+  int r, n_units, hgroups;
+  long long n_wg;
+};
+SparseGrid sparse_grid(const AttnParams& p) {
+  SparseGrid g;
+  g.r = sparse_rows_per_tile(p.H, p.Q);
+  const int B = p.rows / p.Q;
+  g.n_units = B * ((p.Q + g.r - 1) / g.r) * p.splits;
+  const int hp = 32 / g.r;
+  g.hgroups = (p.H + hp - 1) / hp;
+  g.n_wg = (long long)((g.n_units + 7) / 8) * 8 * g.hgroups;
+  return g;
+}
+}  // namespace
+
 int launch_sparse_fp4(const AttnParams& p, hipStream_t stream) {
-  const int hgroups = (p.H + 31) / 32;
-  const int n_units = p.rows * p.splits;
-  const int groups = (n_units + 7) / 8;
-  const long long n_wg = (long long)groups * 8 * hgroups;
-  if (n_wg > 0x7FFFFFFF) return -4;
-  sparse_fp4_kernel<<<dim3((unsigned)n_wg), 256, 0, stream>>>(p, n_units, hgroups);
+  const SparseGrid g = sparse_grid(p);
+  if (g.n_wg > 0x7FFFFFFF) return -4;
+  const dim3 grid((unsigned)g.n_wg);
+  if (g.r == 4)
+    sparse_fp4_kernel<4><<<grid, 256, 0, stream>>>(p, g.n_units, g.hgroups);
+  else if (g.r == 2)
+    sparse_fp4_kernel<2><<<grid, 256, 0, stream>>>(p, g.n_units, g.hgroups);
+  else
+    sparse_fp4_kernel<1><<<grid, 256, 0, stream>>>(p, g.n_units, g.hgroups);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 int launch_attend(const AttnParams& ps, const AttnParams& pw, bool inline_window, hipStream_t stream) {
-  const int hgroups = (ps.H + 31) / 32;
-  const int n_units = ps.rows * ps.splits;
-  const long long n_sparse = (long long)((n_units + 7) / 8) * 8 * hgroups;   // a multiple of 8
+  const SparseGrid g = sparse_grid(ps);
+  const long long n_sparse = g.n_wg;   // a multiple of 8
   const int whgroups = (pw.H + 31) / 32;
-  if (inline_window && (pw.splits > ps.splits || whgroups != hgroups || pw.rows != ps.rows)) return -4;
+  if (inline_window && (g.r != 1 || pw.splits > ps.splits || whgroups != g.hgroups || pw.rows != ps.rows))
+    return -4;
   const long long n_window = inline_window ? 0 : (long long)((pw.rows * pw.splits + 7) / 8) * 8 * whgroups;
   if (n_sparse + n_window > 0x7FFFFFFF) return -4;
-  attend_kernel<<<dim3((unsigned)(n_sparse + n_window)), 256, 0, stream>>>(ps, n_units, hgroups, (int)n_sparse,
-                                                                           pw, whgroups, inline_window ? 1 : 0);
+  const dim3 grid((unsigned)(n_sparse + n_window));
+  const int inl = inline_window ? 1 : 0;
+  if (g.r == 4)
+    attend_kernel<4><<<grid, 256, 0, stream>>>(ps, g.n_units, g.hgroups, (int)n_sparse, pw, whgroups, inl);
+  else if (g.r == 2)
+    attend_kernel<2><<<grid, 256, 0, stream>>>(ps, g.n_units, g.hgroups, (int)n_sparse, pw, whgroups, inl);
+  else
+    attend_kernel<1><<<grid, 256, 0, stream>>>(ps, g.n_units, g.hgroups, (int)n_sparse, pw, whgroups, inl);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -16,6 +16,7 @@ class Config:
     top_groups: int = 0      # two-level indexer: groups kept (0 = flat)
     layers: str = "F"        # cross-layer schedule, e.g. "F R I I" -> "FRII"
     prior: int = 0           # prefill: entries already in the cache before the chunk
+    q_run: int = 1           # prefill: consecutive query rows that share an indexer direction
     seed: int = 0
 
     @property
@@ -39,4 +40,11 @@ CONFIGS = {
                       prior=65536, seed=1004),
     # decode with 3 draft tokens verified in the same pass: 4 query rows per sequence
     "specdec64k": Config("specdec64k", B=32, Q=4, H=64, N=32768, Hi=8, K=2048, W=512, seed=1005),
+    # one GPU's share when the 64 heads are split over 4 GPUs (16 heads each;
+    # the selection is the same on every GPU): the draft rows of specdec64k,
+    # and a prefill chunk whose query tokens come in runs of 64 that ask for
+    # the same context
+    "specdec64k_h16": Config("specdec64k_h16", B=32, Q=4, H=16, N=32768, Hi=8, K=2048, W=512, seed=1005),
+    "prefill_h16": Config("prefill_h16", B=1, Q=4096, H=16, N=67584, Hi=8, K=2048, W=512,
+                          prior=65536, q_run=64, seed=1004),
 }

@@ -255,7 +255,8 @@ def prefill_inputs(cfg, seed=None, q_rows=None, n_dirs=4, c=3.0, beta=1.0):
     """Inputs for a causal chunk: cfg.prior entries already cached, then cfg.Q new raw tokens.
 
     The Q query tokens sit at raw positions 2*prior .. 2*prior + Q - 1; the chunk
-    adds Q/2 new entries.  Queries are split into ``n_dirs`` groups; group d's
+    adds Q/2 new entries.  Queries are split into ``n_dirs`` groups (row r in
+    group (r // cfg.q_run) % n_dirs: runs of q_run consecutive rows); group d's
     indexer queries share a direction v_d (q_idx = z + beta * v_d), and 2048
     blocks per group among the prior blocks get one key bf16(c * v_d).  Returns
     a dict of arrays; ``q_rows`` limits the query rows generated (all positions
@@ -269,7 +270,7 @@ def prefill_inputs(cfg, seed=None, q_rows=None, n_dirs=4, c=3.0, beta=1.0):
     keys = normal_bf16(rng, (1, N, DI))
     dirs = normal_bf16(rng, (n_dirs, DI))
     z = rng.standard_normal((Q, cfg.Hi, DI), dtype=np.float32)
-    group = np.arange(Q) % n_dirs
+    group = (np.arange(Q) // max(int(cfg.q_run), 1)) % n_dirs
     qf = z + np.float32(beta) * bf16_to_f32(dirs)[group][:, None, :]
     q_idx = bf16_rne(qf)[None]
     w = np.abs(rng.standard_normal((1, Q, cfg.Hi), dtype=np.float32)) + np.float32(0.1)
