@@ -183,11 +183,18 @@ int csa2_topk(const float* scores, int rows, int n, int k, int32_t* idx, int32_t
  * dequantised entry; o = softmax(z) V (fp32), lse = log sum exp z.  An empty
  * selection gives o = 0, lse = -inf.  q . K runs on the scaled FP4 x FP6 MFMA
  * (each 32-dim block of the query split into three E2M3 terms that carry it to
- * within 2^-11.7 of the block's largest value, fp32 accumulation); a wave whose
+ * within 2^-11.9 of the block's largest value, fp32 accumulation); a wave whose
  * query blocks spread too far for that (fewer than half of a block's values
- * within 2^4 of its largest) uses two exact E4M3 terms on FP4 x FP8 instead.
- * The softmax weights are rounded to fp16 before the value product with V in
- * fp16.
+ * within 2^5 of its largest) runs q . K on bf16 MFMAs instead, with the codes
+ * dequantised to bf16 (exact) against the bf16 query.  The softmax weights are
+ * rounded to fp16 before the value product with V in fp16.
+ * With 16 or fewer heads (one GPU's share of heads split across GPUs) and
+ * Q >= 2, 2 (H <= 16) or 4 (H <= 8) consecutive rows of a sequence share each
+ * attention tile: the tile attends the union of their selections, every block
+ * gathered and dequantised once for all of them, and each row still sees only
+ * its own blocks, count and causal limit (the results are those of one row
+ * at a time, up to rounding order; a row that lists a block twice counts it
+ * twice, as it does alone).
  *   q bf16 [B][Q][H][512]; cache as above; idx int32 [B][Q][top_k];
  *   count int32 [B][Q]; n_entries int32 [B]; q_pos int32 [B][Q] or NULL
  *   o fp32 [B][Q][H][512]; lse fp32 [B][Q][H] (natural log)

@@ -183,11 +183,28 @@ def test_specdec64k_draft_rows_full_size():
 
 @pytest.mark.timeout(600)
 def test_prefill_sampled_rows():
-    cfg, p, wl = _workload("prefill")
+    _prefill_checks("prefill", sorted(set([0, 4095] + list(np.random.default_rng(4).choice(4096, 62,
+                                                                                           replace=False)))))
+
+
+@pytest.mark.timeout(600)
+def test_row_tiles_full_size():
+    # the head-sharded workloads, where rows share attention tiles: draft rows
+    # (every sequence's 4 rows checked in 8 sequences) and prefill (both rows
+    # of 31 sampled tiles, and the first and last rows)
+    cfg, (x, layers), wl = _workload("specdec64k_h16")
+    _decode_checks(cfg, x, layers, wl, rows=list(range(0, cfg.B, 4)))
+    del wl
+    torch.cuda.empty_cache()
+    pairs = np.random.default_rng(6).choice(2048, 31, replace=False)
+    _prefill_checks("prefill_h16", sorted(set([0, 4095] + [int(r) for k in pairs for r in (2 * k, 2 * k + 1)])))
+
+
+def _prefill_checks(name, rows):
+    cfg, p, wl = _workload(name)
     Q = p["q"].shape[1]
     N, prior = int(p["n_entries"][0]), int(p["prior"])
     nb = cfg.cap // 8
-    rows = sorted(set([0, Q - 1] + list(np.random.default_rng(4).choice(Q, 62, replace=False))))
     idx, cnt = host(wl.buf.idx)[0], host(wl.buf.count)[0]
     out, lse = host(wl.buf.out)[0], host(wl.buf.lse_out)[0]
     exact = 0
@@ -200,8 +217,8 @@ def test_prefill_sampled_rows():
         ro, rl = om.attend_row(p["q"][0, r], rec, idx[r], int(cnt[r]), N, p["swa"][0], int(p["swa_len"][0]),
                                cfg.W, q_pos=t, swa_pos0=int(p["swa_pos0"][0]))
         ref_o.append(ro), ref_l.append(rl)
-    print(f"[full] prefill: {exact} of {len(rows)} sampled rows exact", flush=True)
-    assert_close_rms(out[rows], np.stack(ref_o), what="prefill out")
+    print(f"[full] {name}: {exact} of {len(rows)} sampled rows exact", flush=True)
+    assert_close_rms(out[rows], np.stack(ref_o), what=f"{name} out")
     assert_lse_close(lse[rows], np.stack(ref_l))
     # the chunk's appended records, all 256 blocks: exact bytes
     blocks = np.arange(prior // 8, N // 8)
