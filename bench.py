@@ -650,14 +650,26 @@ _CALL_OF_COMBINE = {"attend_kernel": "csa2_attend_layer", "sparse_fp4_kernel": "
                     "window_kernel": "csa2_swa_merge"}
 
 
-def _kernel_label(name, prev_csa2):
-    """Short label of a dispatch: csa2 kernels without namespace and argument
-    list, the bf16- and MXFP8-key indexers told apart, combine_kernel named by
-    the call it closes (the csa2 kernel dispatched before it)."""
+def _csa2_base(name):
+    """csa2 kernel name without namespace and argument list; the attention
+    kernels also without their rows-per-tile template argument (a workload
+    runs one of them)."""
     base = name.split("(")[0].replace("void ", "").strip()
     if not base.startswith("csa2::"):
         return None
     base = base[len("csa2::"):]
+    if base.startswith(("attend_kernel<", "sparse_fp4_kernel<")):
+        base = base.split("<")[0]
+    return base
+
+
+def _kernel_label(name, prev_csa2):
+    """Short label of a dispatch: csa2 kernels without namespace and argument
+    list, the bf16- and MXFP8-key indexers told apart, combine_kernel named by
+    the call it closes (the csa2 kernel dispatched before it)."""
+    base = _csa2_base(name)
+    if base is None:
+        return None
     if base.startswith("index_scores_kernel") or base.startswith("index_rows_kernel"):
         base += " (MXFP8 keys)" if base.rstrip(">").endswith("true") else " (bf16 keys)"
     if base == "combine_kernel":
@@ -680,7 +692,7 @@ def _labelled(rows):
         lab = _kernel_label(name, prev_csa2)
         if lab is None:
             continue
-        prev_csa2 = name.split("(")[0].replace("void ", "").strip()[len("csa2::"):]
+        prev_csa2 = _csa2_base(name)
         out.append((lab, cold, (en - st) / 1000.0, extra))
     return out
 
