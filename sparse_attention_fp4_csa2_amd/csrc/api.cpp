@@ -307,7 +307,8 @@ int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa
 // its own split count and workgroups after the sparse ones: inline it cost
 // up to ~1 us more there, plus a combine over more splits.
 static bool layer_window_inline(int rows, int Q, int H, int s_sparse, int W) {
-  if (sparse_rows_per_tile(H, Q) > 1) return false;   // row tiles: the window's own workgroups
+  // row tiles: the window on the same tiles, half the work of its own 32-head workgroups
+  if (sparse_rows_per_tile(H, Q) > 1) return true;
   const int wt = (W + 31) / 32;
   const int s_own = window_splits(rows, H, wt);
   return s_sparse >= wt || (wt + s_own - 1) / s_own > 8;

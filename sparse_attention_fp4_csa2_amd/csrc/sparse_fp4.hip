@@ -738,7 +738,8 @@ __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_
 //    them instead of running as short workgroups after them.
 //  * after: the grid is the sparse workgroups followed by the window's, so
 //    the window runs in the slots the sparse workgroups free as they finish.
-// Row tiles (R > 1) take the second arrangement only.
+// Row tiles (R > 1) run the window inline on the same tile of rows (each
+// column over its own row's window); after, on one row per workgroup.
 template <int R>
 __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_units, int hgroups,
                                                         int n_sparse_wg, AttnParams pw, int whgroups,
@@ -756,7 +757,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_uni
     map_unit(blockIdx.x, n_units, hgroups, ps.splits > 1, unit, hgi);
     if (unit >= n_units) return;
     const int row = unit / ps.splits, split = unit - row * ps.splits;
-    if (R == 1 && inline_window && split < pw.splits) {
+    if (inline_window && split < pw.splits) {
       // this workgroup's window split continues the softmax of its sparse
       // split: one partial for both.  The accumulator leaves its V base for
       // plain units first (an exact power of two), as the bf16 window rows
@@ -768,7 +769,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_uni
                     for (int mt = 0; mt < 4; ++mt) oacc[mt] *= rs;
                     base_o = VBIAS;
                     __syncthreads();          // the window reuses the LDS
-                    win::window_tiles(pw, row, split, hgi, lds.w, oacc, m_run, l_lane);
+                    win::window_tiles<R>(pw, row, split, hgi, lds.w, oacc, m_run, l_lane);
                     __syncthreads();          // the epilogue's LDS overlaps the window's
                   });
     } else {
@@ -850,8 +851,7 @@ int launch_attend(const AttnParams& ps, const AttnParams& pw, bool inline_window
   const SparseGrid g = sparse_grid(ps);
   const long long n_sparse = g.n_wg;   // a multiple of 8
   const int whgroups = (pw.H + 31) / 32;
-  if (inline_window && (g.r != 1 || pw.splits > ps.splits || whgroups != g.hgroups || pw.rows != ps.rows))
-    return -4;
+  if (inline_window && (pw.splits > ps.splits || pw.H != ps.H || pw.Q != ps.Q || pw.rows != ps.rows)) return -4;
   const long long n_window = inline_window ? 0 : (long long)((pw.rows * pw.splits + 7) / 8) * 8 * whgroups;
   if (n_sparse + n_window > 0x7FFFFFFF) return -4;
   const dim3 grid((unsigned)(n_sparse + n_window));

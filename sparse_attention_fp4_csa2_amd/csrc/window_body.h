@@ -79,25 +79,53 @@ struct WinRaw {
 // p.splits, head group hgi), continuing the online softmax state it is given:
 // O^T in oacc (plain units), the running max and this lane's denominator.  The
 // fused launch passes the state its sparse share left, so the two branches
-// leave one partial; window_unit starts from an empty state.
+// leave one partial; window_unit starts from an empty state.  R > 1: the
+// sparse kernel's row tile (group `row` of R consecutive rows of a sequence,
+// column e = row e / (32 / R), head (32 / R) hgi + e % (32 / R)); the tiles
+// cover the union of the rows' windows and each column is masked to its own.
+template <int R = 1>
 __device__ __forceinline__ void window_tiles(const AttnParams& p, int row, int split, int hgi, WinLds& lds,
                                              floatx16 (&oacc)[4], float& m_run, float& l_lane) {
+  constexpr int HP = 32 / R;      // heads per row among the 32 columns
   const int tid = threadIdx.x;
   const int dq = tid >> 6;        // wave: latent dims [128dq, 128dq + 128)
   const int lane = tid & 63;
-  const int e = lane & 31;        // Q.K: token of the tile;  S^T, P^T, O^T: head of the group
+  const int e = lane & 31;        // Q.K: token of the tile;  S^T, P^T, O^T: column of the tile
   const int hh = lane >> 5;
-  const int b = row / p.Q;
-  const int head = 32 * hgi + e;
-  const bool head_ok = head < p.H;
+  int b, q0, nr;
+  if (R == 1) {
+    b = row / p.Q;
+    q0 = row - b * p.Q;
+    nr = 1;
+  } else {
+    const int ngq = (p.Q + R - 1) / R;
+    b = row / ngq;
+    q0 = (row - b * ngq) * R;
+    nr = min(R, p.Q - q0);
+  }
+  const int row0 = b * p.Q + q0;
+  const int rsub = e / HP;
+  const int head = HP * hgi + e % HP;
+  const bool head_ok = head < p.H && rsub < nr;
 
-  // ---- visible window slots [lo, lo + n_items) of this row ------------------
+  // ---- visible window slots [lo, lo + n_items) of this row (row tiles: the
+  // union of the rows' visible slots, row r's own being [lo + zlo[r], lo + zhi[r]]) ----
   const int len = min(p.swa_len[b], p.Lw);
   const int pos0 = p.swa_pos0 ? p.swa_pos0[b] : 0;
-  const int tq = p.q_pos ? p.q_pos[row] : pos0 + len - 1;
-  const int za = max(tq - p.W + 1, pos0), zb = min(tq, pos0 + len - 1);
-  const int lo = za - pos0;
+  int za = 0x7FFFFFFF, zb = -0x7FFFFFFF;
+  int zlo[R], zhi[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int tq = r < nr ? (p.q_pos ? p.q_pos[row0 + r] : pos0 + len - 1) : 0;
+    zlo[r] = max(tq - p.W + 1, pos0);
+    zhi[r] = r < nr ? min(tq, pos0 + len - 1) : zlo[r] - 1;
+    if (zhi[r] >= zlo[r]) za = min(za, zlo[r]), zb = max(zb, zhi[r]);
+  }
   const int n_items = zb >= za ? zb - za + 1 : 0;
+  const int lo = n_items ? za - pos0 : 0;
+  if (n_items)
+#pragma unroll
+    for (int r = 0; r < R; ++r) zlo[r] -= za, zhi[r] -= za;
   const int n_tiles = (n_items + TILE - 1) / TILE;
   const int tps = (n_tiles + p.splits - 1) / p.splits;
   const int t_begin = split * tps;
@@ -105,13 +133,27 @@ __device__ __forceinline__ void window_tiles(const AttnParams& p, int row, int s
   const int dim0 = 128 * dq + 64 * hh;      // this lane's 64 contiguous dims
   const float c_log2 = p.scale_log2;
 
-  // ---- query: B operand, lane (head, hh), k-step s: dims dim0 + 8s + [0, 8) ----
+  // ---- query: B operand, lane (column, hh), k-step s: dims dim0 + 8s + [0, 8) ----
   uint4 qf[8];
   {
-    const uint4* src = reinterpret_cast<const uint4*>(p.q + ((size_t)row * p.H + head) * D + dim0);
+    const uint4* src = reinterpret_cast<const uint4*>(
+        p.q + ((size_t)(head_ok ? row0 + rsub : row0) * p.H + (head_ok ? head : 0)) * D + dim0);
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) qf[s8] = head_ok ? src[s8] : make_uint4(0, 0, 0, 0);
   }
+  // the tile's token mask for this lane's column
+  auto tile_mask = [&](int t) -> uint32_t {
+    const bool ok = t < t_end && TILE * t + e < n_items;
+    if (R == 1) return (uint32_t)__ballot(ok);
+    const int sl = TILE * t + e;
+    uint32_t vm = 0;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const uint32_t m = (uint32_t)__ballot(ok && sl >= zlo[k] && sl <= zhi[k]);
+      vm = rsub == k ? m : vm;
+    }
+    return vm;
+  };
 
   // ---- tile helpers -----------------------------------------------------
   // token e of tile t; slots past the split or the window read the row's first
@@ -154,7 +196,7 @@ __device__ __forceinline__ void window_tiles(const AttnParams& p, int row, int s
     fetch(t_begin, rn);
     write_v(rn);
     qk_s(rn);
-    vmask_cur = (uint32_t)__ballot(token_ok(t_begin));
+    vmask_cur = tile_mask(t_begin);
   }
   __syncthreads();
 
@@ -263,7 +305,7 @@ __device__ __forceinline__ void window_tiles(const AttnParams& p, int row, int s
     if (more) {
       write_v(rn);                // after this wave's V^T(t) reads: the LDS keeps their order
       qk_s(rn);
-      vmask_cur = (uint32_t)__ballot(token_ok(t + 1));
+      vmask_cur = tile_mask(t + 1);
       __syncthreads();
     }
   }
