@@ -80,7 +80,7 @@ struct AttnParams {
 int window_splits(int rows, int H, int n_tiles);
 int launch_window(const AttnParams& p, hipStream_t stream);
 // MXFP4 selected blocks (sparse_fp4.hip): 32-head workgroups, two per CU
-int sparse_fp4_splits(int rows, int H, int n_tiles);
+int sparse_fp4_splits(int rows, int H, int n_tiles, int stage);   // stage: block ids a split stages
 // rows per tile (1, 2 or 4: with 16 or fewer heads, rows of a sequence share
 // the tile's columns and its gathers) and the split count of a sparse launch
 int sparse_rows_per_tile(int H, int Q);

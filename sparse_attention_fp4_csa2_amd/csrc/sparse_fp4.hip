@@ -52,6 +52,10 @@ namespace {
 constexpr int TILE = 32;                 // entries per tile
 constexpr int PROW = 40;                 // fp16 slots per P row (32 entries + 8 pad)
 constexpr int MAX_SPLIT_BLOCKS = 2048;   // selected block ids one workgroup stages in LDS
+// row tiles stage twice as many (the union of up to R selections), so that a
+// tile of two rows needs no second split for the K = 2048 of each
+template <int R>
+constexpr int stage_blocks() { return R > 1 ? 2 * MAX_SPLIT_BLOCKS : MAX_SPLIT_BLOCKS; }
 constexpr float LAZY_LOG2 = 8.0f;        // move the running max only when it grows by > 2^8
 constexpr float M_INIT = -1.0e30f;       // finite "no max yet": exp2(x - M_INIT) never NaN
 constexpr int VBIAS = 140;               // V' = V * 2^(VBIAS - vbase): code 6 at vbase -> 6*2^13
@@ -59,6 +63,7 @@ constexpr int VBIAS = 140;               // V' = V * 2^(VBIAS - vbase): code 6 a
 typedef int int32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 
+template <int R>
 struct Lds {
   union {
     floatx4 sp[2][4][4][64];       // [buffer][wave][quarter][lane] partial S^T  32 KB
@@ -69,8 +74,8 @@ struct Lds {
   int flag[2][4];                  // [buffer][wave] quarter needs a max move
   float lsum[4][32];               // epilogue: per-wave softmax denominators
   int emax[4][32];                 // epilogue: per-wave exponent of the largest |o|
-  int32_t blk[MAX_SPLIT_BLOCKS];   // this split's selected block ids           8 KB
-  uint8_t memb[MAX_SPLIT_BLOCKS];  // row tiles: bit r = row r of the tile selected the item
+  int32_t blk[stage_blocks<R>()];  // this split's selected block ids           8 KB (row tiles 16 KB)
+  uint8_t memb[R > 1 ? stage_blocks<R>() : 4];   // row tiles: bit r = row r of the tile selected the item
   uint32_t scan[4];                // row tiles: per-wave sums of the union count
   int dup;                         // row tiles: some row lists a block twice
 };
@@ -160,7 +165,7 @@ constexpr int BUF_DWORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
 // before the epilogue, and may continue the softmax state (the fused launch
 // runs its window share there, so both branches leave one partial).
 template <int R, typename AfterLoop>
-__device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int split, int hgi, Lds& lds,
+__device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int split, int hgi, Lds<R>& lds,
                                             AfterLoop after_loop) {
   constexpr int HP = 32 / R;      // heads per row among the tile's 32 columns
   const int tid = threadIdx.x;
@@ -217,11 +222,11 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
   const float c_log2 = p.scale_log2;
   auto read_id = [&](int t) -> int {
     const int item = 4 * t + (e >> 3);
-    return item < n_items_split ? lds.blk[min(item - 4 * t_begin, MAX_SPLIT_BLOCKS - 1)] : -1;
+    return item < n_items_split ? lds.blk[min(item - 4 * t_begin, stage_blocks<R>() - 1)] : -1;
   };
   auto read_mb = [&](int t) -> int {
     const int item = 4 * t + (e >> 3);
-    return R > 1 && item < n_items_split ? lds.memb[min(item - 4 * t_begin, MAX_SPLIT_BLOCKS - 1)] : 0;
+    return R > 1 && item < n_items_split ? lds.memb[min(item - 4 * t_begin, stage_blocks<R>() - 1)] : 0;
   };
   auto fetch = [&](int blk, int mb, Raw& r) {
     const int ent = blk * BLOCK + (e & 7);
@@ -716,7 +721,7 @@ __device__ __forceinline__ void sparse_unit(const AttnParams& p, int row, int sp
 // R rows per tile (1, 2, 4); a unit is (tile, split)
 template <int R>
 __global__ __launch_bounds__(256, 2) void sparse_fp4_kernel(AttnParams p, int n_units, int hgroups) {
-  __shared__ Lds lds;
+  __shared__ Lds<R> lds;
   // every argument the prologue needs, in one round of scalar loads: left to
   // itself the compiler loads them in three dependent rounds, each waited on
   // where it is first used (the early return splits the prologue)
@@ -745,7 +750,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_uni
                                                         int n_sparse_wg, AttnParams pw, int whgroups,
                                                         int inline_window) {
   __shared__ union {
-    Lds s;
+    Lds<R> s;
     win::WinLds w;
   } lds;
   // every argument the sparse prologue needs, in one round of scalar loads (as
@@ -783,7 +788,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(AttnParams ps, int n_uni
   }
 }
 
-int sparse_fp4_splits(int rows, int H, int n_tiles) {
+int sparse_fp4_splits(int rows, int H, int n_tiles, int stage) {
   const int hgroups = (H + 31) / 32;
   const int wgs = rows * hgroups;
   int s = (512 + wgs - 1) / wgs;                 // two workgroups per CU
@@ -791,7 +796,7 @@ int sparse_fp4_splits(int rows, int H, int n_tiles) {
   if (s > cap_by_tiles) s = cap_by_tiles;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
-  const int min_s = (n_tiles + MAX_SPLIT_BLOCKS / 4 - 1) / (MAX_SPLIT_BLOCKS / 4);
+  const int min_s = (n_tiles + stage / 4 - 1) / (stage / 4);   // each split's share fits the staging
   if (s < min_s) s = min_s;
   return s;
 }
@@ -813,7 +818,8 @@ int sparse_attn_splits(int B, int Q, int H, int top_k) {
   const int r = sparse_rows_per_tile(H, Q);
   const int tiles = B * ((Q + r - 1) / r);
   const int hp = 32 / r;
-  return sparse_fp4_splits(tiles * ((H + hp - 1) / hp), 32, (r * top_k + 3) / 4);
+  return sparse_fp4_splits(tiles * ((H + hp - 1) / hp), 32, (r * top_k + 3) / 4,
+                           r > 1 ? stage_blocks<2>() : stage_blocks<1>());
 }
 
 namespace {
