@@ -37,9 +37,10 @@
 //  * workgroup order: each XCD takes a contiguous range of (row, split, head
 //    group), so a row's query and (between its two head groups) its records
 //    are read from HBM once and then hit that XCD's L2.
-//  * of the two workgroups on a CU the older one wins instruction arbitration
-//    and finishes far ahead of the other; waves drop their priority on every
-//    other tile, which evens out the two.
+//  * row tiles: with 16 or fewer heads a row leaves columns of the tile idle,
+//    so 2 or 4 rows of one sequence share them (see sparse_unit) and attend
+//    the union of their selections, each block gathered and dequantised once
+//    for all of them.
 #include "device.h"
 #include "launch.h"
 #include "select.h"
@@ -143,7 +144,7 @@ __device__ __forceinline__ int wave_max_int(int v) {
 struct Raw {
   uint4 c0, c1;    // 32 bytes of codes: this wave's dims 64s + 32hh + [0, 32), s = 0, 1
   uint32_t sc;     // scale bytes of groups 4dq .. 4dq + 3
-  int valid;       // the entry is present and visible; row tiles: bit r = to row r of the tile
+  int valid;       // the entry is present and visible; row tiles: bit r = visible to row r of the tile
 };
 
 constexpr int BUF_DWORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
