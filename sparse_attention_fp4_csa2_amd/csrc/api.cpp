@@ -264,7 +264,7 @@ int csa2_sparse_attn(const uint16_t* q, const uint8_t* cache, const int32_t* idx
 size_t csa2_swa_merge_ws(int B, int Q, int H, int W) {
   if (B <= 0 || Q <= 0 || H <= 0 || W <= 0) return 0;
   const int rows = B * Q;
-  const int s = window_splits(rows, H, (W + 31) / 32);
+  const int s = window_attn_splits(B, Q, H, W);
   return part_ws_layout(rows, s, H).total;
 }
 
@@ -283,7 +283,7 @@ int csa2_swa_merge(const uint16_t* q, const uint16_t* swa_kv, const int32_t* swa
   if (!ws || ws_bytes < need) return CSA2_ERR_WS_TOO_SMALL;
   if (!aligned(ws, WS_ALIGN)) return CSA2_ERR_INVALID_ARG;
   const int rows = B * Q;
-  const int splits = window_splits(rows, H, (W + 31) / 32);
+  const int splits = window_attn_splits(B, Q, H, W);
   AttnParams p{};
   p.q = q; p.swa = swa_kv; p.swa_len = swa_len; p.swa_pos0 = swa_pos0; p.W = W; p.Lw = Lw;
   p.q_pos = q_pos; p.Q = Q; p.H = H; p.rows = rows; p.splits = splits;

@@ -17,12 +17,14 @@
 
 namespace csa2 {
 
-__global__ __launch_bounds__(256, 2) void window_kernel(AttnParams p, int hgroups) {
+// R rows per tile (1, 2, 4: as the sparse kernel's row tiles); a unit is (tile, split)
+template <int R>
+__global__ __launch_bounds__(256, 2) void window_kernel(AttnParams p, int n_units, int hgroups) {
   __shared__ win::WinLds lds;
   int unit, hgi;
-  map_unit(blockIdx.x, p.rows * p.splits, hgroups, p.splits > 1, unit, hgi);
-  if (unit >= p.rows * p.splits) return;
-  win::window_unit(p, unit / p.splits, unit % p.splits, hgi, lds);
+  map_unit(blockIdx.x, n_units, hgroups, p.splits > 1, unit, hgi);
+  if (unit >= n_units) return;
+  win::window_unit<R>(p, unit / p.splits, unit % p.splits, hgi, lds);
 }
 
 int window_splits(int rows, int H, int n_tiles) {
@@ -36,12 +38,27 @@ int window_splits(int rows, int H, int n_tiles) {
   return s;
 }
 
+// the rule above over a launch's tiles: rows, or row tiles of 32 / R heads
+int window_attn_splits(int B, int Q, int H, int W) {
+  const int r = sparse_rows_per_tile(H, Q);
+  const int hp = 32 / r;
+  return window_splits(B * ((Q + r - 1) / r) * ((H + hp - 1) / hp), 32, (W + 31) / 32);
+}
+
 int launch_window(const AttnParams& p, hipStream_t stream) {
-  const int hgroups = (p.H + 31) / 32;
-  const int n_units = p.rows * p.splits;
+  const int r = sparse_rows_per_tile(p.H, p.Q);
+  const int hp = 32 / r;
+  const int hgroups = (p.H + hp - 1) / hp;
+  const int n_units = (p.rows / p.Q) * ((p.Q + r - 1) / r) * p.splits;
   const long long n_wg = (long long)((n_units + 7) / 8) * 8 * hgroups;
   if (n_wg > 0x7FFFFFFF) return -4;
-  window_kernel<<<dim3((unsigned)n_wg), 256, 0, stream>>>(p, hgroups);
+  const dim3 grid((unsigned)n_wg);
+  if (r == 4)
+    window_kernel<4><<<grid, 256, 0, stream>>>(p, n_units, hgroups);
+  else if (r == 2)
+    window_kernel<2><<<grid, 256, 0, stream>>>(p, n_units, hgroups);
+  else
+    window_kernel<1><<<grid, 256, 0, stream>>>(p, n_units, hgroups);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

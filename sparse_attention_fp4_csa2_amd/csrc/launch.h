@@ -78,6 +78,8 @@ struct AttnParams {
 
 // bf16 window (attention.hip): 32-head workgroups, few tiles per row
 int window_splits(int rows, int H, int n_tiles);
+// split count of a window launch over B sequences of Q rows (row tiles as in the sparse kernel)
+int window_attn_splits(int B, int Q, int H, int W);
 int launch_window(const AttnParams& p, hipStream_t stream);
 // MXFP4 selected blocks (sparse_fp4.hip): 32-head workgroups, two per CU
 int sparse_fp4_splits(int rows, int H, int n_tiles, int stage);   // stage: block ids a split stages

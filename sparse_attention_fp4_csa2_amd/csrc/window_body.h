@@ -313,20 +313,30 @@ __device__ __forceinline__ void window_tiles(const AttnParams& p, int row, int s
 }
 
 // One workgroup's share: row `row`, split `split` of p.splits, head group hgi
+// (R > 1: the row tile `row`, its columns as in window_tiles)
+template <int R = 1>
 __device__ __forceinline__ void window_unit(const AttnParams& p, int row, int split, int hgi, WinLds& lds) {
+  constexpr int HP = 32 / R;
   const int tid = threadIdx.x;
   const int dq = tid >> 6;
   const int lane = tid & 63;
   const int e = lane & 31;
   const int hh = lane >> 5;
-  const int head = 32 * hgi + e;
-  const bool head_ok = head < p.H;
+  int row_l = row, nr = 1;
+  if (R > 1) {
+    const int ngq = (p.Q + R - 1) / R;
+    const int b = row / ngq, q0 = (row - b * ngq) * R;
+    nr = min(R, p.Q - q0);
+    row_l = b * p.Q + q0 + e / HP;
+  }
+  const int head = HP * hgi + e % HP;
+  const bool head_ok = head < p.H && e / HP < nr;
   floatx16 oacc[4];       // O^T: [dims 128dq + 32mt + 8(i/4) + 4hh + i%4][head]
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) oacc[mt] = floatx16{};
   float m_run = M_INIT;   // running max of z * log2(e), per head (lane pair)
   float l_lane = 0.f;     // softmax denominator over this lane's quarter tokens
-  window_tiles(p, row, split, hgi, lds, oacc, m_run, l_lane);
+  window_tiles<R>(p, row, split, hgi, lds, oacc, m_run, l_lane);
 
   // ---- finalize: denominators across the 4 quarter owners -----------------
   const float lq = pair_sum(l_lane);
@@ -334,7 +344,7 @@ __device__ __forceinline__ void window_unit(const AttnParams& p, int row, int sp
   __syncthreads();
   const float l = (lds.lsum[0][e] + lds.lsum[1][e]) + (lds.lsum[2][e] + lds.lsum[3][e]);
   const float il = l > 0.f ? 1.f / l : 0.f;
-  const size_t orow = ((size_t)row * p.H + head) * p.out_splits + p.split_base + split;
+  const size_t orow = ((size_t)row_l * p.H + head) * p.out_splits + p.split_base + split;
   if (head_ok && dq == 0 && hh == 0) {
     const float lse = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
     p.lse_out[orow] = lse;

@@ -6,8 +6,8 @@ limit, its count): checked against the fp64 oracle row by row, at the same bar
 as the single-row tiles (max|err| <= 1e-2 x RMS, lse within 1e-3).  Covered:
 overlapping and disjoint selections, ragged and empty counts, out-of-range ids,
 causal rows, a short last group, duplicate ids and caches too large for the
-union's bitmap (both run the rows' lists one after the other), and the
-one-call layer with its window branch.
+union's bitmap (both run the rows' lists one after the other), the one-call
+layer with its window branch, and the standalone window call on row tiles.
 """
 
 import numpy as np
@@ -155,5 +155,37 @@ def test_row_tiles_attend_layer(H, Q):
         for r in range(Q):
             ro, rl = modes.attend_row(q[b, r], cache_np[b], idx[b, r], int(count[b, r]), N, swa[b], Lw, W,
                                       q_pos=int(q_pos[b, r]), swa_pos0=pos0)
+            assert_close_rms(out[b, r], ro, what=f"row ({b}, {r})")
+            assert_lse_close(lse[b, r], rl)
+
+
+@pytest.mark.parametrize("H,Q", [(16, 3), (8, 4)])
+def test_row_tiles_swa_merge(H, Q):
+    # the standalone window call on row tiles: causal rows of one sequence at
+    # different positions (their windows overlap only in part), one sequence
+    # with a short window; merged with the oracle's sparse branch
+    rng = rng_for(760 + H)
+    B, N, K, W, Lw = 2, 1024, 24, 96, 160
+    lat = normal_bf16(rng, (B, N, 512))
+    cache_np = [mxfp4.build_records(lat[b], N) for b in range(B)]
+    q = normal_bf16(rng, (B, Q, H, 512))
+    swa = normal_bf16(rng, (B, Lw, 512))
+    swa_len = np.array([Lw, 40], np.int32)
+    pos0 = np.array([2 * N - 100, 2 * N - 30], np.int32)
+    q_pos = np.stack([2 * N - 100 + 37 * np.arange(Q) + 50, 2 * N - 30 + np.arange(Q) + 5]).astype(np.int32)
+    idx, count = _selections(rng, B, Q, N // 8, K, shared=12, extra=12)
+    o_s = np.zeros((B, Q, H, 512))
+    l_s = np.zeros((B, Q, H))
+    for b in range(B):
+        for r in range(Q):
+            o1, l1 = oracle_rows(q[b:b + 1, r:r + 1], cache_np[b][None], idx[b:b + 1, r:r + 1],
+                                 count[b:b + 1, r:r + 1], [N], q_pos[b:b + 1, r:r + 1])
+            o_s[b, r], l_s[b, r] = o1[0, 0], l1[0, 0]
+    from tests.test_gpu_attention import gpu_swa
+    out, lse = gpu_swa(q, swa, swa_len, W, o_s, l_s, swa_pos0=pos0, q_pos=q_pos)
+    for b in range(B):
+        for r in range(Q):
+            ro, rl = modes.attend_row(q[b, r], cache_np[b], idx[b, r], int(count[b, r]), N, swa[b],
+                                      int(swa_len[b]), W, q_pos=int(q_pos[b, r]), swa_pos0=int(pos0[b]))
             assert_close_rms(out[b, r], ro, what=f"row ({b}, {r})")
             assert_lse_close(lse[b, r], rl)
