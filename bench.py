@@ -652,13 +652,13 @@ _CALL_OF_COMBINE = {"attend_kernel": "csa2_attend_layer", "sparse_fp4_kernel": "
 
 def _csa2_base(name):
     """csa2 kernel name without namespace and argument list; the attention
-    kernels also without their rows-per-tile template argument (a workload
-    runs one of them)."""
+    and window kernels also without their rows-per-tile template argument (a
+    workload runs one of each)."""
     base = name.split("(")[0].replace("void ", "").strip()
     if not base.startswith("csa2::"):
         return None
     base = base[len("csa2::"):]
-    if base.startswith(("attend_kernel<", "sparse_fp4_kernel<")):
+    if base.startswith(("attend_kernel<", "sparse_fp4_kernel<", "window_kernel<")):
         base = base.split("<")[0]
     return base
 
