@@ -109,3 +109,20 @@ def test_workspace_sizes_are_pure_and_monotone(lib):
     assert b >= 8 * 256 * 64 * 4 + 8 * 1024 * 4 + 8 * 256 * 4 + 8 * 4
     assert lib.csa2_swa_merge_ws(32, 1, 64, 512) >= lib.csa2_swa_merge_ws(1, 1, 64, 512)
     assert lib.csa2_index_topk_ws(0, 1, 8, 0) == 0
+
+
+def test_layer_plan_with_row_tiles(lib):
+    # host-side plan of a layer call (no GPU).  With 16 or fewer heads and
+    # several rows per sequence, rows share attention tiles: a 4096-row
+    # prefill chunk then runs one split per two-row tile with the window on the
+    # same tiles, so its layer is one launch, as at 64 heads; 4 draft rows per
+    # sequence need split-K and a combine (two launches), as do Q = 1 decode
+    # rows, which keep one row per tile
+    B, K, W = 1, 2048, 512
+    assert lib.csa2_attend_layer_launches(B, 4096, 64, K, W) == 1
+    assert lib.csa2_attend_layer_launches(B, 4096, 16, K, W) == 1
+    assert lib.csa2_attend_layer_launches(32, 4, 16, K, W) == 2
+    assert lib.csa2_attend_layer_launches(32, 1, 16, K, W) == 2
+    # a one-split call needs no workspace; a split one does
+    assert lib.csa2_sparse_attn_ws(B, 4096, 16, K) == 0
+    assert lib.csa2_sparse_attn_ws(32, 4, 16, K) > 0
