@@ -47,8 +47,6 @@ IndexWs index_ws_layout(int B, int Q, int cap, int top_groups) {
   return l;
 }
 
-int attn_n_tiles(int top_k) { return (top_k + 3) / 4; }
-
 // Split-K partials of the attention calls: fp16 o [rows][H][splits][512],
 // int32 exponent and fp32 lse [rows][H][splits] (a (row, head)'s splits adjacent).
 struct PartWs {
